@@ -1,0 +1,98 @@
+"""The oracle against routes that do not go through it (CPU only).
+
+Brute force, torch fp64 SDPA, closed forms, invariants, split/combine and the
+append are in ``pins.py``; the hand-derived example is in
+``golden/hand_example.json``.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import pins
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+def test_brute_force():
+    pins.pin_brute_force(oracle)
+
+
+def test_sdpa_library_route():
+    pins.pin_sdpa(oracle)
+
+
+def test_closed_forms():
+    pins.pin_closed_forms(oracle)
+
+
+def test_invariants():
+    pins.pin_invariants(oracle)
+
+
+def test_combine_partition_invariance():
+    pins.pin_combine(oracle)
+
+
+def test_append_matches_history_layout():
+    pins.pin_append(oracle)
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("layer", ["full", "ring"])
+def test_hand_example_attention(layer):
+    g = _golden()
+    c = g[layer]
+    W = c.get("window", 0)
+    q = np.array(g["q"], dtype=np.float64)
+    out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
+                                  np.array(c["v_pool_after"], dtype=np.float64),
+                                  np.array(c["block_table"]), np.array(c["seq_lens"]),
+                                  np.array(g["sinks"]), W)
+    np.testing.assert_allclose(out, np.array(c["expected_out"]), rtol=0, atol=1e-12)
+    if "expected_out_no_sinks" in c:
+        out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
+                                      np.array(c["v_pool_after"], dtype=np.float64),
+                                      np.array(c["block_table"]), np.array(c["seq_lens"]),
+                                      None, W)
+        np.testing.assert_allclose(out, np.array(c["expected_out_no_sinks"]), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("layer", ["full", "ring"])
+def test_hand_example_append(layer):
+    g = _golden()
+    c = g[layer]
+    k, v = oracle.kv_append(np.array(c["k_pool_before"]), np.array(c["v_pool_before"]),
+                            np.array(c["k_new"]), np.array(c["v_new"]),
+                            np.array(c["block_table"]), np.array(c["seq_lens"]),
+                            c.get("window", 0))
+    assert np.array_equal(k, np.array(c["k_pool_after"]))
+    assert np.array_equal(v, np.array(c["v_pool_after"]))
+
+
+def test_bf16_widening_exact():
+    # 1.0, -2.0, 0.15625, the largest finite bf16, the smallest subnormal, -0
+    bits = np.array([0x3F80, 0xC000, 0x3E20, 0x7F7F, 0x0001, 0x8000], dtype=np.uint16)
+    want = [1.0, -2.0, 0.15625, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133, -0.0]
+    got = oracle.bf16_bits_to_f64(bits)
+    assert list(got) == want
+    assert math.copysign(1.0, got[-1]) == -1.0
+
+
+def test_empty_context_and_no_sink_gives_zero():
+    q = np.ones((1, 2, 4))
+    kp = np.ones((2, 1, 2, 4))
+    vp = np.ones((2, 1, 4, 2))
+    out = oracle.decode_attention(q, kp, vp, np.array([[0]]), np.array([0]), None, 0)
+    assert np.array_equal(out, np.zeros((1, 2, 4)))
+    # a finite sink with no positions also gives 0 (the sink has no value row)
+    out = oracle.decode_attention(q, kp, vp, np.array([[0]]), np.array([0]), np.zeros(2), 0)
+    assert np.array_equal(out, np.zeros((1, 2, 4)))
