@@ -1,0 +1,183 @@
+/*
+ * sa.h -- single-token decode attention over a paged / ring KV cache on
+ * AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * Sources.  The SimpleLLM README (shadowgraph.io/naklecha/simple-llm),
+ * optimisation table: one fused decode-attention kernel covers attention
+ * sinks, sliding-window attention, GQA and the KV append; full-attention
+ * layers keep a paged KV cache; sliding-window layers keep a ring buffer.
+ * The "learn-llm-inference-from-scratch" setup page, file table: KV cache
+ * (S05), PagedAttention (S06) and FlashAttention (S12) chapters.  The pages
+ * print no formula; the definitions below are the standard ones for those
+ * concepts.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Every pointer is DEVICE memory owned by the caller, except the
+ *    `const sa_dims*`, which is host memory read during the call only.
+ *    The library never allocates, frees or synchronises; it keeps no
+ *    global mutable state and is safe to call from several host threads.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    null stream).  A return of SA_OK means the work was enqueued; a fault
+ *    inside a kernel surfaces as a HIP error at the caller's next
+ *    synchronisation.
+ *  - Errors are negative SA_ERR_* codes returned before anything is
+ *    launched; no call aborts or throws.
+ *  - Shapes: B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0,
+ *    Hq/Hkv <= 16), head_dim D == 64, block_size bs in {8, 16, 32, 64}.
+ *  - GQA: query head h reads KV head h / (Hq/Hkv) (contiguous groups).
+ *  - Layouts (row-major, innermost last; bf16 = IEEE bfloat16 bits):
+ *      q, out          bf16 [B][Hq][D]
+ *      k_new, v_new    bf16 [B][Hkv][D]
+ *      k_cache         bf16 [num_blocks][Hkv][bs][D]
+ *      v_cache         bf16 [num_blocks][Hkv][D][bs]   (V transposed in a block)
+ *      block_table     int32 [B][max_blocks_per_seq]
+ *      seq_lens        int32 [B]
+ *      sinks           fp32 [Hq] (may be NULL: no sink)
+ *      part_o          fp32 [B][Hq][S][D]
+ *      part_lse        fp32 [B][Hq][S]        (natural log)
+ *  - seq_lens[b] = L is the context length AFTER this step's append: the
+ *    new token is position L-1.  The same array feeds append and attention.
+ *  - window <= 0: full-attention layer; position p lives in slot p.
+ *    window  = W > 0: sliding-window layer kept as a ring of W slots;
+ *    position p lives in slot p mod W and the query attends to positions
+ *    [max(0, L-W), L), i.e. slots [0, min(L, W)).  ceil(W/bs) must not
+ *    exceed max_blocks_per_seq.
+ *  - Slot s of sequence b lives in block block_table[b][s / bs] at offset
+ *    s % bs.  Only the table entries that cover attended slots are read.
+ *    A context longer than max_blocks_per_seq*bs is cut to that capacity.
+ *    Table entries outside [0, num_blocks) are clamped into range by the
+ *    attention kernels and skipped by the append (a caller error, but
+ *    never a wild access).
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t sa_bf16;   /* bfloat16 bit pattern */
+
+typedef struct sa_dims {
+    int32_t num_seqs;            /* B   (0 is a no-op)                          */
+    int32_t num_q_heads;         /* Hq                                          */
+    int32_t num_kv_heads;        /* Hkv                                         */
+    int32_t head_dim;            /* D: 64                                       */
+    int32_t block_size;          /* bs: 8, 16, 32 or 64 tokens per block        */
+    int32_t max_blocks_per_seq;  /* row stride of block_table                   */
+    int32_t num_blocks;          /* blocks in each pool                         */
+    int32_t num_splits;          /* 0: the library's fixed split table;
+                                    > 0: use at most this many split-K
+                                    partitions per (sequence, KV head)         */
+    int32_t variant;             /* 0: default kernels; see SA_VARIANT_*        */
+} sa_dims;
+
+enum {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = -1,    /* NULL pointer, negative or inconsistent size  */
+    SA_ERR_UNSUPPORTED = -2,    /* D != 64, Hq % Hkv != 0, Hq/Hkv > 16, bs, ... */
+    SA_ERR_WORKSPACE = -3,      /* workspace missing or too small               */
+    SA_ERR_HIP = -4             /* the HIP runtime refused a launch             */
+};
+
+/* Kernel variants (sa_dims.variant).  All give results within the same
+ * tolerance; they exist so each design choice can be measured. */
+enum {
+    SA_VARIANT_DEFAULT = 0,
+    SA_VARIANT_MFMA_TWO_PASS = 1, /* MFMA partitions, separate combine launch  */
+    SA_VARIANT_MFMA_FUSED = 2,    /* MFMA partitions, combine by the last one  */
+    SA_VARIANT_VALU = 3           /* vector-ALU partitions (no MFMA)           */
+};
+
+/*
+ * KV append (SimpleLLM README, optimisation table: the fused kernel's KV
+ * append; paged-cache and ring-buffer rows for where the token goes).
+ * For every sequence b with L = seq_lens[b] >= 1 and every KV head g, writes
+ * k_new[b][g][:] to k_cache[blk][g][off][:] and v_new[b][g][:] to
+ * v_cache[blk][g][:][off], where slot s = L-1 (window <= 0) or (L-1) mod W,
+ * blk = block_table[b][s / bs], off = s % bs.  A bit copy: nothing else in
+ * either pool changes.  Sequences with L <= 0 are skipped.
+ * Uses: num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+ * num_blocks.
+ */
+int sa_kv_append(const sa_bf16* k_new, const sa_bf16* v_new,
+                 sa_bf16* k_cache, sa_bf16* v_cache,
+                 const int32_t* block_table, const int32_t* seq_lens,
+                 int32_t window, const sa_dims* dims, void* stream);
+
+/*
+ * Split-K partitions S the attention call uses for these dims and window
+ * (>= 1), or a negative SA_ERR_* code.  Deterministic: it depends only on
+ * the dims, the window and num_splits, never on timing.
+ */
+int32_t sa_decode_num_splits(const sa_dims* dims, int32_t window);
+
+/*
+ * Device workspace bytes sa_decode_attention needs for these dims and window
+ * (0 when it needs none, also returned for invalid dims).  The workspace
+ * must be zero-filled once before its first use; every call leaves it ready
+ * for the next (its counters return to zero).  Calls that may run at the
+ * same time need workspaces of their own.
+ */
+size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window);
+
+/*
+ * Decode attention (SimpleLLM README, optimisation table: sinks, sliding
+ * window and GQA in one decode-attention kernel; paged cache and ring
+ * buffer; the tutorial's PagedAttention and FlashAttention chapters for the
+ * block-table read and the tiled online softmax).  For every sequence b and
+ * query head h, with scores s_p = q[b][h] . K_p / sqrt(D) over the attended
+ * positions p and sink logit sigma_h = sinks[h] (-inf if sinks is NULL):
+ *
+ *     M = max(max_p s_p, sigma_h)
+ *     out[b][h] = sum_p e^(s_p - M) V_p / (sum_p e^(s_p - M) + e^(sigma_h - M))
+ *
+ * rounded to bf16 (round to nearest even); 0 where nothing is attended.
+ * Accumulation is fp32.  Long contexts are cut into S split-K partitions
+ * whose partials are merged with a log-sum-exp combine inside the call.
+ * workspace: at least sa_decode_workspace_bytes(dims, window) bytes (may be
+ * NULL when that is 0), zero-filled before first use.
+ */
+int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const float* sinks, int32_t window, sa_bf16* out,
+                        const sa_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Split-K partials only, for a caller that merges them itself (for example
+ * across devices that each hold part of a context).  With S =
+ * sa_decode_num_splits(dims, window), partition j of (b, h) covers attended
+ * slots [j*P, min(n, (j+1)*P)) for the library's partition length P, and
+ *     part_lse[b][h][j] = log sum_p e^(s_p)          (-inf if empty)
+ *     part_o[b][h][j][:] = sum_p e^(s_p) V_p / e^(part_lse)
+ * No sink is applied.  part_o of an empty partition is left unwritten.
+ */
+int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       int32_t window, float* part_o, float* part_lse,
+                       const sa_dims* dims, void* stream);
+
+/*
+ * Log-sum-exp combine of num_splits partials per (b, h) with the sink:
+ *     M = max(max_j part_lse[b][h][j], sigma_h)
+ *     out[b][h] = sum_j e^(lse_j - M) part_o[b][h][j] / (sum_j e^(lse_j - M) + e^(sigma_h - M))
+ * rounded to bf16; partials with lse = -inf are skipped (their part_o is
+ * never read); 0 where nothing remains.  Uses num_seqs, num_q_heads and
+ * head_dim of dims.
+ */
+int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
+               int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream);
+
+/* Static text for a status code. */
+const char* sa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

@@ -1,0 +1,273 @@
+"""Python binding of libsa: paged GQA decode attention for MI355X (gfx950).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of ``libsa.so`` behind the C ABI declared in ``include/sa.h``.  PyTorch
+supplies device memory and streams; this module checks that tensors have the
+documented dtypes, shapes and layouts, derives ``sa_dims`` from them, passes
+raw device pointers and the current HIP stream, and turns a negative status
+into an exception.  There is no fallback: without the built library every
+call raises.
+
+Layouts (see include/sa.h): q/out ``[B][Hq][D]`` bf16; k_new/v_new
+``[B][Hkv][D]`` bf16; k_cache ``[NB][Hkv][bs][D]`` bf16; v_cache
+``[NB][Hkv][D][bs]`` bf16; block_table ``[B][MBS]`` int32; seq_lens ``[B]``
+int32 (length after the append); sinks ``[Hq]`` fp32 or None.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsa.so")
+
+SA_OK = 0
+VARIANT_DEFAULT = 0
+VARIANT_MFMA_TWO_PASS = 1
+VARIANT_MFMA_FUSED = 2
+VARIANT_VALU = 3
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("variant", ctypes.c_int32),
+    ]
+
+
+class SAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+_lib = None
+EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
+           "sa_decode_attention", "sa_decode_partials", "sa_combine", "sa_status_string")
+
+
+def load(path: Optional[str] = None):
+    """Load libsa.so (built by ``python -m paged_gqa_decode_step_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with "
+                          "`python -m paged_gqa_decode_step_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(p)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    dp = ctypes.POINTER(Dims)
+    lib.sa_kv_append.argtypes = [vp, vp, vp, vp, vp, vp, i32, dp, vp]
+    lib.sa_kv_append.restype = ctypes.c_int
+    lib.sa_decode_num_splits.argtypes = [dp, i32]
+    lib.sa_decode_num_splits.restype = i32
+    lib.sa_decode_workspace_bytes.argtypes = [dp, i32]
+    lib.sa_decode_workspace_bytes.restype = sz
+    lib.sa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, dp, vp, sz, vp]
+    lib.sa_decode_attention.restype = ctypes.c_int
+    lib.sa_decode_partials.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, dp, vp]
+    lib.sa_decode_partials.restype = ctypes.c_int
+    lib.sa_combine.argtypes = [vp, vp, vp, i32, vp, dp, vp]
+    lib.sa_combine.restype = ctypes.c_int
+    lib.sa_status_string.argtypes = [ctypes.c_int]
+    lib.sa_status_string.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().sa_status_string(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _cache_dims(k_cache, v_cache, block_table, B, num_splits, variant):
+    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(v_cache, "v_cache", torch.bfloat16, 4, k_cache.device)
+    _check(block_table, "block_table", torch.int32, 2, k_cache.device)
+    NB, Hkv, bs, D = k_cache.shape
+    if tuple(v_cache.shape) != (NB, Hkv, D, bs):
+        raise ValueError(f"v_cache must be [NB][Hkv][D][bs] = {(NB, Hkv, D, bs)}, "
+                         f"got {tuple(v_cache.shape)}")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    return Dims(B, 0, Hkv, D, bs, block_table.shape[1], NB, int(num_splits), int(variant))
+
+
+def dims_for(q, k_cache, v_cache, block_table, num_splits=0, variant=VARIANT_DEFAULT) -> Dims:
+    _check(q, "q", torch.bfloat16, 3)
+    d = _cache_dims(k_cache, v_cache, block_table, q.shape[0], num_splits, variant)
+    d.num_q_heads = q.shape[1]
+    if q.shape[2] != d.head_dim:
+        raise ValueError("q and the caches disagree on head_dim")
+    return d
+
+
+def _raise(st: int, what: str):
+    if st != SA_OK:
+        raise SAError(st, what)
+
+
+# ---------------------------------------------------------------------------
+# the C-ABI calls
+# ---------------------------------------------------------------------------
+
+def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, window=0, stream=None):
+    """Write each sequence's new K/V row into its paged block or ring slot."""
+    _check(k_new, "k_new", torch.bfloat16, 3, k_cache.device)
+    _check(v_new, "v_new", torch.bfloat16, 3, k_cache.device)
+    _check(seq_lens, "seq_lens", torch.int32, 1, k_cache.device)
+    B = k_new.shape[0]
+    d = _cache_dims(k_cache, v_cache, block_table, B, 0, 0)
+    if tuple(k_new.shape) != (B, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if seq_lens.shape[0] != B:
+        raise ValueError("seq_lens must have one entry per sequence")
+    d.num_q_heads = d.num_kv_heads
+    st = load().sa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(block_table), _ptr(seq_lens), int(window),
+                             ctypes.byref(d), _stream(stream))
+    _raise(st, "sa_kv_append")
+
+
+def num_splits(q, k_cache, v_cache, block_table, window=0, num_splits=0,
+               variant=VARIANT_DEFAULT) -> int:
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    s = load().sa_decode_num_splits(ctypes.byref(d), int(window))
+    _raise(min(s, 0), "sa_decode_num_splits")
+    return int(s)
+
+
+def workspace_bytes(q, k_cache, v_cache, block_table, window=0, num_splits=0,
+                    variant=VARIANT_DEFAULT) -> int:
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    return int(load().sa_decode_workspace_bytes(ctypes.byref(d), int(window)))
+
+
+def new_workspace(q, k_cache, v_cache, block_table, window=0, num_splits=0,
+                  variant=VARIANT_DEFAULT) -> Optional[torch.Tensor]:
+    """A zero-filled device workspace of the size the call needs (None if 0)."""
+    n = workspace_bytes(q, k_cache, v_cache, block_table, window, num_splits, variant)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+
+
+def decode_attention(q, k_cache, v_cache, block_table, seq_lens, sinks=None, window=0,
+                     out=None, workspace=None, num_splits=0, variant=VARIANT_DEFAULT,
+                     stream=None):
+    """Decode attention over the paged cache (window <= 0) or ring (window > 0).
+
+    Returns ``out`` (bf16 ``[B][Hq][D]``).  ``workspace`` must be a zeroed
+    uint8 device tensor of at least ``workspace_bytes(...)`` bytes when that
+    is non-zero; one is allocated if none is given.
+    """
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    dev = q.device
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != d.num_q_heads:
+            raise ValueError("sinks must have one entry per query head")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                    _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out),
+                                    ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream))
+    _raise(st, "sa_decode_attention")
+    return out
+
+
+def decode_partials(q, k_cache, v_cache, block_table, seq_lens, window=0, num_splits=0,
+                    part_o=None, part_lse=None, stream=None):
+    """Split-K partials ``(part_o [B][Hq][S][D], part_lse [B][Hq][S])`` without sink."""
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, VARIANT_DEFAULT)
+    dev = q.device
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    S = load().sa_decode_num_splits(ctypes.byref(d), int(window))
+    _raise(min(S, 0), "sa_decode_num_splits")
+    B, Hq, D = q.shape
+    if part_o is None:
+        part_o = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    _check(part_o, "part_o", torch.float32, 4, dev)
+    _check(part_lse, "part_lse", torch.float32, 3, dev)
+    if tuple(part_o.shape) != (B, Hq, S, D) or tuple(part_lse.shape) != (B, Hq, S):
+        raise ValueError(f"partials must be [B][Hq][{S}][D] and [B][Hq][{S}]")
+    st = load().sa_decode_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                   _ptr(seq_lens), int(window), _ptr(part_o), _ptr(part_lse),
+                                   ctypes.byref(d), _stream(stream))
+    _raise(st, "sa_decode_partials")
+    return part_o, part_lse
+
+
+def combine(part_o, part_lse, sinks=None, out=None, stream=None):
+    """Log-sum-exp combine of ``[B][Hq][S][D]`` partials with the sink."""
+    _check(part_o, "part_o", torch.float32, 4)
+    dev = part_o.device
+    _check(part_lse, "part_lse", torch.float32, 3, dev)
+    B, Hq, S, D = part_o.shape
+    if tuple(part_lse.shape) != (B, Hq, S):
+        raise ValueError("part_lse must be [B][Hq][S]")
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != Hq:
+            raise ValueError("sinks must have one entry per query head")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+    _check(out, "out", torch.bfloat16, 3, dev)
+    d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0)
+    st = load().sa_combine(_ptr(part_o), _ptr(part_lse), _ptr(sinks), int(S), _ptr(out),
+                           ctypes.byref(d), _stream(stream))
+    _raise(st, "sa_combine")
+    return out

@@ -1,0 +1,267 @@
+// C-ABI layer of libsa: argument checks, the fixed split table, launches.
+//
+// Nothing here allocates, frees or synchronises; every call checks its
+// arguments completely before it enqueues any kernel on the caller's stream.
+#include <limits.h>
+#include <math.h>
+
+#include "../../include/sa.h"
+#include "sa_internal.h"
+
+namespace {
+
+using sa::kHeadDim;
+
+// Fixed split table (no autotuning, so the result of a call never depends on
+// timing): partitions are 32 * 2^k slots, at most kMaxTableSlice blocks and
+// at most kMaxPartTokens slots long, and shrink until every call has about
+// kTargetWaves partition wavefronts (8 per compute unit of an MI355X).
+constexpr int kMaxPartTokens = 1024;
+constexpr long kTargetWaves = 2048;
+// The last partition of a (b, g) merges the partials itself while there are
+// at most this many; beyond it a separate combine launch is used.
+constexpr int kMaxFusedSplits = 32;
+// Whether the default variant fuses the combine (when kMaxFusedSplits allows).
+constexpr bool kFuseByDefault = false;
+
+int log2_exact(int x) {
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return (1 << l) == x ? l : -1;
+}
+
+int check_dims(const sa_dims* d, int32_t window) {
+    if (!d) return SA_ERR_INVALID_ARG;
+    if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
+        d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->num_splits < 0 ||
+        d->head_dim < 1 || d->block_size < 1)
+        return SA_ERR_INVALID_ARG;
+    if (d->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
+    if (d->num_q_heads % d->num_kv_heads) return SA_ERR_UNSUPPORTED;
+    if (d->num_q_heads / d->num_kv_heads > sa::kMaxGroup) return SA_ERR_UNSUPPORTED;
+    const int l = log2_exact(d->block_size);
+    if (l < 3 || l > 6) return SA_ERR_UNSUPPORTED;
+    if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_VALU) return SA_ERR_INVALID_ARG;
+    if (window > 0 && (window + d->block_size - 1) / d->block_size > d->max_blocks_per_seq)
+        return SA_ERR_INVALID_ARG;
+    if ((long long)d->num_blocks * d->num_kv_heads * d->block_size * kHeadDim > (1LL << 40))
+        return SA_ERR_INVALID_ARG;
+    return SA_OK;
+}
+
+struct Plan {
+    int32_t splits;
+    int32_t part_tokens;
+};
+
+// Assumes check_dims passed.
+Plan plan(const sa_dims* d, int32_t window) {
+    const int bs = d->block_size;
+    const long cap = (long)d->max_blocks_per_seq * bs;
+    const long max_n = window > 0 ? (window < cap ? window : cap) : cap;
+    const int gran = bs > sa::kStepTokens ? bs : sa::kStepTokens;
+    int pmax = sa::kMaxTableSlice * bs;
+    if (pmax > kMaxPartTokens && kMaxPartTokens >= gran) pmax = kMaxPartTokens;
+    int P;
+    if (d->num_splits > 0) {
+        long want = (max_n + d->num_splits - 1) / d->num_splits;
+        want = (want + gran - 1) / gran * gran;
+        P = (int)(want < gran ? gran : (want > pmax ? pmax : want));
+    } else {
+        const long units = (long)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
+        P = pmax;
+        while (P / 2 >= gran && units * ((max_n + P - 1) / P) < kTargetWaves) P /= 2;
+    }
+    Plan p;
+    p.part_tokens = P;
+    p.splits = (int32_t)((max_n + P - 1) / P);
+    return p;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WorkspaceLayout {
+    size_t part_o, part_lse, counters, total;
+};
+
+WorkspaceLayout workspace_layout(const sa_dims* d, int32_t splits) {
+    WorkspaceLayout w{};
+    if (splits <= 1) return w;
+    const size_t bh = (size_t)d->num_seqs * d->num_q_heads;
+    w.part_o = 0;
+    w.part_lse = align256(bh * splits * kHeadDim * sizeof(float));
+    w.counters = w.part_lse + align256(bh * splits * sizeof(float));
+    w.total = w.counters + align256((size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t));
+    return w;
+}
+
+bool grid_fits(const sa_dims* d, int32_t splits) {
+    return (long long)d->num_seqs * d->num_kv_heads * splits < INT_MAX;
+}
+
+sa::DecodeArgs decode_args(const sa_dims* d, int32_t window, const Plan& p) {
+    sa::DecodeArgs a{};
+    a.B = d->num_seqs;
+    a.Hq = d->num_q_heads;
+    a.Hkv = d->num_kv_heads;
+    a.G = d->num_q_heads / d->num_kv_heads;
+    a.bs_log2 = log2_exact(d->block_size);
+    a.mbs = d->max_blocks_per_seq;
+    a.num_blocks = d->num_blocks;
+    a.window = window > 0 ? window : 0;
+    a.num_splits = p.splits;
+    a.part_tokens = p.part_tokens;
+    a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)kHeadDim));
+    return a;
+}
+
+int to_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int sa_kv_append(const sa_bf16* k_new, const sa_bf16* v_new, sa_bf16* k_cache,
+                 sa_bf16* v_cache, const int32_t* block_table, const int32_t* seq_lens,
+                 int32_t window, const sa_dims* dims, void* stream) {
+    int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
+        return SA_ERR_INVALID_ARG;
+    if ((long long)dims->num_seqs * dims->num_kv_heads >= INT_MAX) return SA_ERR_INVALID_ARG;
+    sa::AppendArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.B = dims->num_seqs;
+    a.Hkv = dims->num_kv_heads;
+    a.bs_log2 = log2_exact(dims->block_size);
+    a.mbs = dims->max_blocks_per_seq;
+    a.num_blocks = dims->num_blocks;
+    a.window = window > 0 ? window : 0;
+    return to_status(sa::launch_kv_append(a, (hipStream_t)stream));
+}
+
+int32_t sa_decode_num_splits(const sa_dims* dims, int32_t window) {
+    const int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    return plan(dims, window).splits;
+}
+
+size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window) {
+    if (check_dims(dims, window) != SA_OK) return 0;
+    return workspace_layout(dims, plan(dims, window).splits).total;
+}
+
+int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const float* sinks, int32_t window, sa_bf16* out,
+                        const sa_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return SA_ERR_INVALID_ARG;
+    if (dims->variant == SA_VARIANT_VALU) return SA_ERR_UNSUPPORTED;
+    const Plan p = plan(dims, window);
+    if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
+    const WorkspaceLayout wl = workspace_layout(dims, p.splits);
+    if (wl.total && (!workspace || workspace_bytes < wl.total)) return SA_ERR_WORKSPACE;
+
+    sa::DecodeArgs a = decode_args(dims, window, p);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.sinks = sinks;
+    a.out = out;
+    hipStream_t s = (hipStream_t)stream;
+    if (p.splits == 1) {
+        a.mode = sa::kWriteOut;
+        return to_status(sa::launch_decode_mfma(a, s));
+    }
+    char* ws = (char*)workspace;
+    a.part_o = (float*)(ws + wl.part_o);
+    a.part_lse = (float*)(ws + wl.part_lse);
+    a.counters = (int32_t*)(ws + wl.counters);
+    const bool fused = dims->variant == SA_VARIANT_MFMA_FUSED ||
+                       (dims->variant == SA_VARIANT_DEFAULT && kFuseByDefault &&
+                        p.splits <= kMaxFusedSplits);
+    if (fused) {
+        a.mode = sa::kFusedCombine;
+        return to_status(sa::launch_decode_mfma(a, s));
+    }
+    a.mode = sa::kWritePartials;
+    st = to_status(sa::launch_decode_mfma(a, s));
+    if (st != SA_OK) return st;
+    sa::CombineArgs c{};
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.sinks = sinks;
+    c.out = out;
+    c.B = a.B;
+    c.Hq = a.Hq;
+    c.num_splits = p.splits;
+    return to_status(sa::launch_combine(c, s));
+}
+
+int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
+                       const int32_t* block_table, const int32_t* seq_lens, int32_t window,
+                       float* part_o, float* part_lse, const sa_dims* dims, void* stream) {
+    int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_lse)
+        return SA_ERR_INVALID_ARG;
+    if (dims->variant == SA_VARIANT_VALU) return SA_ERR_UNSUPPORTED;
+    const Plan p = plan(dims, window);
+    if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
+    sa::DecodeArgs a = decode_args(dims, window, p);
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.seq_lens = seq_lens;
+    a.part_o = part_o;
+    a.part_lse = part_lse;
+    a.mode = sa::kWritePartials;
+    return to_status(sa::launch_decode_mfma(a, (hipStream_t)stream));
+}
+
+int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
+               int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream) {
+    if (!dims) return SA_ERR_INVALID_ARG;
+    if (dims->num_seqs < 0 || dims->num_q_heads < 1 || num_splits < 1) return SA_ERR_INVALID_ARG;
+    if (dims->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!part_o || !part_lse || !out) return SA_ERR_INVALID_ARG;
+    if ((long long)dims->num_seqs * dims->num_q_heads >= INT_MAX) return SA_ERR_INVALID_ARG;
+    sa::CombineArgs c{};
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.sinks = sinks;
+    c.out = out;
+    c.B = dims->num_seqs;
+    c.Hq = dims->num_q_heads;
+    c.num_splits = num_splits;
+    return to_status(sa::launch_combine(c, (hipStream_t)stream));
+}
+
+const char* sa_status_string(int status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID_ARG: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported shape";
+        case SA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SA_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Internal interface between the C-ABI layer (sa_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+constexpr int kHeadDim = 64;       // D handled by the kernels
+constexpr int kMaxGroup = 16;      // query heads per KV head (one MFMA column tile)
+constexpr int kStepTokens = 32;    // tokens per inner step of the partition kernels
+constexpr int kMaxTableSlice = 64; // block-table entries one partition may span
+
+struct AppendArgs {
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    int32_t B, Hkv, bs_log2, mbs, num_blocks, window;
+};
+
+// What a partition kernel does with its result.
+enum PartitionMode : int32_t {
+    kWriteOut = 0,        // S == 1: apply the sink, write bf16 out
+    kWritePartials = 1,   // write (o, lse) partials; empty partitions write lse = -inf
+    kFusedCombine = 2,    // write partials; the last partition of a (b, g) merges them
+};
+
+struct DecodeArgs {
+    const uint16_t* q;
+    const uint16_t* k_cache;
+    const uint16_t* v_cache;
+    const int32_t* block_table;
+    const int32_t* seq_lens;
+    const float* sinks;       // may be null
+    uint16_t* out;            // kWriteOut, kFusedCombine
+    float* part_o;            // kWritePartials, kFusedCombine
+    float* part_lse;
+    int32_t* counters;        // kFusedCombine: [B*Hkv], zero between calls
+    int32_t B, Hq, Hkv, G;
+    int32_t bs_log2, mbs, num_blocks, window;
+    int32_t num_splits;       // S
+    int32_t part_tokens;      // P: slots per partition (multiple of 32 and of bs)
+    int32_t mode;             // PartitionMode
+    float scale_log2;         // log2(e) / sqrt(D)
+};
+
+struct CombineArgs {
+    const float* part_o;
+    const float* part_lse;
+    const float* sinks;       // may be null
+    uint16_t* out;
+    int32_t B, Hq, num_splits;
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports what include/sa.h declares,
+and rejects bad arguments with its status codes before launching anything.
+
+No call here reaches a kernel launch: every case fails validation first, so
+these run without a GPU (the pointers passed are never dereferenced).
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_decode_step_amd as sa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE = -1, -2, -3
+FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sa.load()
+
+
+def good_dims(**kw):
+    d = dict(num_seqs=2, num_q_heads=16, num_kv_heads=2, head_dim=64, block_size=16,
+             max_blocks_per_seq=8, num_blocks=32, num_splits=0, variant=0)
+    d.update(kw)
+    return sa.Dims(**d)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
+    assert set(names) == set(sa.EXPORTS)
+
+
+def test_status_strings(lib):
+    assert sa.status_string(0) == "ok"
+    for s in (-1, -2, -3, -4):
+        assert sa.status_string(s) not in ("ok", "unknown status")
+    assert sa.status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=128), SA_ERR_UNSUPPORTED),
+    (dict(num_q_heads=12, num_kv_heads=8), SA_ERR_UNSUPPORTED),   # Hq % Hkv
+    (dict(num_q_heads=64, num_kv_heads=2), SA_ERR_UNSUPPORTED),   # G = 32 > 16
+    (dict(block_size=12), SA_ERR_UNSUPPORTED),
+    (dict(block_size=4), SA_ERR_UNSUPPORTED),
+    (dict(block_size=128), SA_ERR_UNSUPPORTED),
+    (dict(num_seqs=-1), SA_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), SA_ERR_INVALID_ARG),
+    (dict(max_blocks_per_seq=0), SA_ERR_INVALID_ARG),
+    (dict(num_blocks=0), SA_ERR_INVALID_ARG),
+    (dict(num_splits=-2), SA_ERR_INVALID_ARG),
+    (dict(variant=9), SA_ERR_INVALID_ARG),
+])
+def test_bad_dims_rejected_everywhere(lib, kw, status):
+    d = good_dims(**kw)
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == status
+    assert lib.sa_decode_workspace_bytes(ctypes.byref(d), 0) == 0
+    assert lib.sa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(d), None) == status
+    assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE,
+                                   ctypes.byref(d), FAKE, 1 << 30, None) == status
+    assert lib.sa_decode_partials(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE,
+                                  ctypes.byref(d), None) == status
+
+
+def test_window_needs_room_in_the_table(lib):
+    d = good_dims(max_blocks_per_seq=4)
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 64) >= 1
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 65) == SA_ERR_INVALID_ARG
+
+
+def test_null_dims_and_pointers(lib):
+    assert lib.sa_decode_num_splits(None, 0) == SA_ERR_INVALID_ARG
+    d = good_dims()
+    assert lib.sa_kv_append(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(d), None) \
+        == SA_ERR_INVALID_ARG
+    for i in range(6):
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.sa_kv_append(*args, 0, ctypes.byref(d), None) == SA_ERR_INVALID_ARG
+    # sinks (index 5) may be NULL; every other pointer may not
+    for i in (0, 1, 2, 3, 4):
+        args = [FAKE] * 6
+        args[i] = None
+        assert lib.sa_decode_attention(*args, 0, FAKE, ctypes.byref(d), FAKE, 1 << 30,
+                                       None) == SA_ERR_INVALID_ARG
+    assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None,
+                                   ctypes.byref(d), FAKE, 1 << 30, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_combine(None, FAKE, FAKE, 4, FAKE, ctypes.byref(d), None) == SA_ERR_INVALID_ARG
+    assert lib.sa_combine(FAKE, FAKE, FAKE, 0, FAKE, ctypes.byref(d), None) == SA_ERR_INVALID_ARG
+    assert lib.sa_combine(FAKE, FAKE, FAKE, 4, FAKE, None, None) == SA_ERR_INVALID_ARG
+
+
+def test_workspace_too_small(lib):
+    d = good_dims(max_blocks_per_seq=512, num_splits=4)
+    need = lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
+    assert need > 0
+    assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                   ctypes.byref(d), FAKE, need - 1, None) == SA_ERR_WORKSPACE
+    assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE,
+                                   ctypes.byref(d), None, need, None) == SA_ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_noop(lib):
+    d = good_dims(num_seqs=0)
+    assert lib.sa_kv_append(None, None, None, None, None, None, 0, ctypes.byref(d), None) == 0
+    assert lib.sa_decode_attention(None, None, None, None, None, None, 0, None,
+                                   ctypes.byref(d), None, 0, None) == 0
+
+
+def test_split_table_is_fixed_and_bounded(lib):
+    # the headline shape: batch 64, 64/8 heads, 8192-slot capacity
+    d = good_dims(num_seqs=64, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=512,
+                  num_blocks=64 * 512 + 1)
+    s = lib.sa_decode_num_splits(ctypes.byref(d), 0)
+    assert s == lib.sa_decode_num_splits(ctypes.byref(d), 0)
+    assert 1 <= s <= 8192 // 32
+    # a ring of 128 slots never needs more than 4 partitions of 32
+    assert 1 <= lib.sa_decode_num_splits(ctypes.byref(d), 128) <= 4
+    # forced split counts: never more partitions than asked, never < 32 slots each
+    for want in (1, 2, 7, 32, 256, 1000):
+        d.num_splits = want
+        s = lib.sa_decode_num_splits(ctypes.byref(d), 0)
+        assert 1 <= s <= max(want, 8192 // 1024) and s <= 8192 // 32
+    d.num_splits = 1
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == 8   # partitions are at most 1024 slots

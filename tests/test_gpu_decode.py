@@ -1,0 +1,247 @@
+"""Decode attention on the GPU against the fp64 oracle (max-abs <= 2e-2,
+mean-abs <= 2e-3), through the C ABI.  Sizes span several partitions and a
+ragged tail; the full-size workloads are checked in test_gpu_workloads.py."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tails
+
+pytestmark = pytest.mark.gpu
+
+VARIANTS = [0, 1, 2]
+
+
+def attend(lib, layer, num_splits=0, variant=0, sinks="layer"):
+    s = layer.sinks if sinks == "layer" else sinks
+    out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                               layer.seq_lens, s, layer.window, num_splits=num_splits,
+                               variant=variant)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("L", [38, 37])
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_tiny_config_with_append(lib, L, variant):
+    """batch 1, 4 query heads / 1 KV head, D 64, bs 16, shuffled table, sinks,
+    one new token appended (L = 38 reads 37 cached + 1 new; 37 also run)."""
+    cfg = dict(synth.CONFIGS["tiny"], lens=[L])
+    layer = synth.make_layer(device="cuda", **cfg)
+    ref = oracle_attention(layer, after_append=True)
+    lib.kv_append(layer.k_new, layer.v_new, layer.k_cache, layer.v_cache,
+                  layer.block_table, layer.seq_lens, 0)
+    assert_parity(out_f64(attend(lib, layer, variant=variant)), ref, f"tiny L={L}")
+
+
+@pytest.mark.parametrize("scale", [0.125, 1.0])
+def test_gptoss_layer_8k(lib, scale):
+    cfg = dict(synth.CONFIGS["gptoss_layer_8k"], scale=scale)
+    layer = synth.make_layer(device="cuda", **cfg)
+    ref = oracle_attention(layer)
+    for v in VARIANTS:
+        assert_parity(out_f64(attend(lib, layer, variant=v)), ref, f"8k scale={scale} v={v}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 7, 32, 256])
+def test_split_sweep(lib, S):
+    layer = synth.make_layer(batch=3, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[8192, 3001, 77], seed=300 + S, device="cuda")
+    ref = oracle_attention(layer)
+    for v in VARIANTS:
+        got = out_f64(attend(lib, layer, num_splits=S, variant=v))
+        assert_parity(got, ref, f"S={S} variant={v}")
+
+
+@pytest.mark.parametrize("W", [128, 100])
+def test_window_edges(lib, W):
+    lens = [1, W - 1, W, W + 1, 2 * W + 3, 5000]
+    layer = synth.make_layer(batch=len(lens), q_heads=64, kv_heads=8, head_dim=64,
+                             block_size=16, lens=lens, window=W, seed=400 + W, device="cuda")
+    ref = oracle_attention(layer, after_append=True)
+    lib.kv_append(layer.k_new, layer.v_new, layer.k_cache, layer.v_cache,
+                  layer.block_table, layer.seq_lens, W)
+    for v in VARIANTS:
+        for S in (0, 1, 3):
+            assert_parity(out_f64(attend(lib, layer, num_splits=S, variant=v)), ref,
+                          f"W={W} S={S} v={v}")
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32, 64])
+def test_block_sizes(lib, bs):
+    lens = [1, 31, 32, 33, 1000, 2049]
+    layer = synth.make_layer(batch=len(lens), q_heads=32, kv_heads=4, head_dim=64,
+                             block_size=bs, lens=lens, seed=500 + bs, device="cuda")
+    ref = oracle_attention(layer)
+    for S in (0, 1, 5):
+        assert_parity(out_f64(attend(lib, layer, num_splits=S)), ref, f"bs={bs} S={S}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
+def test_group_sizes(lib, G):
+    layer = synth.make_layer(batch=2, q_heads=4 * G, kv_heads=4, head_dim=64, block_size=16,
+                             lens=[700, 129], seed=600 + G, device="cuda")
+    ref = oracle_attention(layer)
+    assert_parity(out_f64(attend(lib, layer)), ref, f"G={G}")
+
+
+def test_no_sinks_is_plain_softmax(lib):
+    layer = synth.make_layer(batch=4, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[1, 17, 300, 2000], seed=700, device="cuda", sinks=False)
+    ref = oracle_attention(layer)
+    got = out_f64(attend(lib, layer))
+    assert_parity(got, ref, "no sinks")
+    # L = 1 without a sink returns v0 exactly (bf16 of it)
+    v0 = bits(layer.v_cache)[int(layer.block_table[0, 0]), :, :, 0]   # [Hkv][D]
+    v0 = oracle.bf16_bits_to_f64(v0)
+    assert np.array_equal(got[0], np.repeat(v0, 8, axis=0))
+    # sinks of -inf equal no sinks, bit for bit
+    neg = torch.full((64,), -math.inf, device="cuda")
+    assert torch.equal(attend(lib, layer, sinks=neg), attend(lib, layer, sinks=None))
+
+
+def test_large_sinks_and_scores(lib):
+    """Sinks far above and below the scores, and large-magnitude queries."""
+    layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=[50, 900, 4000], seed=710, device="cuda", scale=3.0)
+    layer.sinks = torch.tensor([60.0, -60.0, 0.0, 5.0] * 4, device="cuda")
+    ref = oracle_attention(layer)
+    for v in VARIANTS:
+        assert_parity(out_f64(attend(lib, layer, variant=v)), ref, f"large v={v}")
+
+
+def test_paged_equals_contiguous_bitwise(lib):
+    """The same cache contents through a shuffled and an identity table give
+    bit-identical outputs at a fixed split count."""
+    layer = synth.make_layer(batch=4, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[40, 999, 4096, 123], seed=800, device="cuda")
+    bt = layer.block_table.cpu()
+    order = []
+    for b, n in enumerate(layer.blocks_per_seq):
+        order.extend(bt[b, :n].tolist())
+    order.append(layer.poison_block)
+    idx = torch.as_tensor(order, device="cuda")
+    k2 = layer.k_cache.index_select(0, idx).contiguous()
+    v2 = layer.v_cache.index_select(0, idx).contiguous()
+    bt2 = torch.full_like(layer.block_table, len(order) - 1)
+    start = 0
+    for b, n in enumerate(layer.blocks_per_seq):
+        bt2[b, :n] = torch.arange(start, start + n, dtype=torch.int32)
+        start += n
+    for v in VARIANTS:
+        for S in (0, 4):
+            a = attend(lib, layer, num_splits=S, variant=v)
+            c = lib.decode_attention(layer.q, k2, v2, bt2, layer.seq_lens, layer.sinks, 0,
+                                     num_splits=S, variant=v)
+            torch.cuda.synchronize()
+            assert torch.equal(a, c), f"paged != contiguous (S={S}, v={v})"
+
+
+def test_deterministic(lib):
+    layer = synth.make_layer(batch=8, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=synth.ragged_lengths(9, 8, 100, 6000).tolist(), seed=900,
+                             device="cuda")
+    for v in VARIANTS:
+        a = attend(lib, layer, variant=v)
+        b = attend(lib, layer, variant=v)
+        assert torch.equal(a, b), f"variant {v} not deterministic"
+
+
+def test_stale_nan_tails_never_leak(lib):
+    """NaN in every slot past each sequence's end (inside its own blocks) and
+    the poison block behind unused table entries never reach the output."""
+    for W in (0, 128):
+        layer = synth.make_layer(batch=5, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                                 lens=[1, 15, 33, 100, 1001], window=W, seed=950 + W,
+                                 device="cuda")
+        ref = oracle_attention(layer)
+        poison_tails(layer)
+        for v in VARIANTS:
+            for S in (0, 1, 3):
+                assert_parity(out_f64(attend(lib, layer, num_splits=S, variant=v)), ref,
+                              f"NaN tails W={W} S={S} v={v}")
+
+
+def test_empty_context_gives_zero(lib):
+    layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=[5, 64, 300], seed=990, device="cuda")
+    layer.seq_lens[1] = 0
+    for v in VARIANTS:
+        for S in (0, 1, 4):
+            out = attend(lib, layer, num_splits=S, variant=v)
+            assert torch.count_nonzero(out[1]) == 0
+    ref = oracle_attention(layer)
+    assert_parity(out_f64(attend(lib, layer)), ref, "with an empty sequence")
+
+
+def test_partials_and_combine_entry_points(lib):
+    layer = synth.make_layer(batch=3, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[10, 3000, 8192], seed=1000, device="cuda")
+    po, pl = lib.decode_partials(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                                 layer.seq_lens, 0, num_splits=16)
+    torch.cuda.synchronize()
+    S = po.shape[2]
+    assert S >= 8
+    # every non-empty partial against the oracle's partial over the same slots;
+    # the partition length is the capacity split S ways, rounded up to 32 slots
+    cap = layer.max_blocks_per_seq * layer.block_size
+    P = math.ceil(math.ceil(cap / S) / 32) * 32
+    assert math.ceil(cap / P) == S
+    sl = synth.to_bits
+    q, k, v, bt = sl(layer.q), sl(layer.k_cache), sl(layer.v_cache), sl(layer.block_table)
+    lse = pl.cpu().numpy()
+    o = po.cpu().numpy()
+    for b, L in enumerate(layer.seq_lens.cpu().tolist()):
+        for h in (0, 7, 8, 63):
+            for j in range(S):
+                lo, hi = j * P, min(L, (j + 1) * P)
+                if lo >= L:
+                    assert lse[b, h, j] == -np.inf
+                    continue
+                ro, rl = oracle.partial_attention(q, k, v, bt, b, h, range(lo, hi), 0)
+                assert abs(lse[b, h, j] - rl) < 1e-3 * max(1.0, abs(rl))
+                assert np.abs(o[b, h, j] - ro).max() < 1e-2
+    out = lib.combine(po, pl, layer.sinks)
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), oracle_attention(layer), "partials + combine")
+
+
+def test_combine_alone(lib):
+    """sa_combine on random partials, some empty (-inf), against the oracle."""
+    g = torch.Generator().manual_seed(5)
+    B, Hq, S, D = 3, 8, 9, 64
+    po = torch.randn(B, Hq, S, D, generator=g)
+    pl = torch.randn(B, Hq, S, generator=g) * 4
+    pl[0, :, 3] = -math.inf
+    pl[1, 2, :] = -math.inf            # a head with nothing: only the sink
+    pl[2, 5, :] = -math.inf
+    po[0, :, 3] = float("nan")        # never read
+    sinks = torch.randn(Hq, generator=g)
+    ref = oracle.combine(po.numpy(), pl.numpy(), sinks.numpy())
+    out = lib.combine(po.cuda(), pl.cuda(), sinks.cuda())
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), ref, "combine")
+    out = lib.combine(po.cuda(), pl.cuda(), None)
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), oracle.combine(po.numpy(), pl.numpy(), None), "combine no sink")
+    assert torch.count_nonzero(out[1, 2]) == 0
+
+
+def test_workspace_reused_across_calls(lib):
+    """One zeroed workspace serves many fused calls of different shapes."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    for i, lens in enumerate(([5000, 17, 8000], [1, 2, 3], [4097, 4096, 9000])):
+        layer = synth.make_layer(batch=3, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                                 lens=lens, seed=1100 + i, device="cuda")
+        ref = oracle_attention(layer)
+        for S in (0, 5, 16):
+            out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                                       layer.seq_lens, layer.sinks, 0, workspace=ws,
+                                       num_splits=S, variant=2)
+            torch.cuda.synchronize()
+            assert_parity(out_f64(out), ref, f"reuse {i} S={S}")
