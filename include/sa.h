@@ -118,10 +118,12 @@ int32_t sa_decode_num_splits(const sa_dims* dims, int32_t window);
 
 /*
  * Device workspace bytes sa_decode_attention needs for these dims and window
- * (0 when it needs none, also returned for invalid dims).  The workspace
- * must be zero-filled once before its first use; every call leaves it ready
- * for the next (its counters return to zero).  Calls that may run at the
- * same time need workspaces of their own.
+ * (0 when it needs none, also returned for invalid dims).  The first 256 KiB
+ * of a workspace hold completion counters: zero-fill the workspace once
+ * before its first use; every call leaves those counters at zero again, so
+ * one workspace of the largest size needed serves any sequence of calls on a
+ * stream, whatever their dims.  Calls that may run at the same time need
+ * workspaces of their own.
  */
 size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window);
 

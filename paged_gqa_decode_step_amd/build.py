@@ -44,9 +44,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libsa.so")
 
 
-def _compile(src: str, obj: str, verbose: bool) -> None:
+def _compile(src: str, obj: str, verbose: bool, extra=()) -> None:
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + FLAGS + lang + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + FLAGS + list(extra) + lang + ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,31 +58,40 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(err, file=sys.stderr)
 
 
-def build(jobs: int = 8, verbose: bool = False) -> str:
-    """Compile every source under csrc/ and link libsa.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int = 8, verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source under csrc/ and link ``out`` (default: the
+    package's libsa.so); returns its path.  ``defines`` are extra ``-D``
+    settings of the kernels' build-time tuning knobs (SA_PIPE, SA_KV_NT), for
+    building side-by-side variants to measure."""
+    tag = "".join(d.replace("=", "") for d in defines)
+    bdir = os.path.join(BUILD, tag) if tag else BUILD
+    os.makedirs(bdir, exist_ok=True)
+    extra = [f"-D{d}" for d in defines]
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
-    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
+    objs = [os.path.join(bdir, os.path.basename(s) + ".o") for s in srcs]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        for f in [ex.submit(_compile, s, o, verbose) for s, o in zip(srcs, objs)]:
+        for f in [ex.submit(_compile, s, o, verbose, extra) for s, o in zip(srcs, objs)]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--jobs", type=int, default=8)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="tuning knob, e.g. -D SA_PIPE=3 (use with --out)")
+    ap.add_argument("--out", default=LIB, help="output library path")
     args = ap.parse_args()
-    print(build(args.jobs, args.verbose))
+    print(build(args.jobs, args.verbose, args.defines, args.out))
 
 
 if __name__ == "__main__":

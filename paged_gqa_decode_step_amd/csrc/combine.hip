@@ -7,8 +7,13 @@
 // V) and lse_j = log sum e^s over its slots.  With M = max(max_j lse_j, sigma_h)
 //     out = sum_j e^(lse_j - M) o_j / (sum_j e^(lse_j - M) + e^(sigma_h - M)).
 // Partials with lse = -inf (empty partitions) carry no weight and are never
-// read.  One wavefront per (b, h); lane = dimension, so every partial row is
-// one coalesced 256-byte load.
+// read.
+//
+// One workgroup per (b, h) with WAVES wavefronts: every wavefront finds M over
+// all partials (lanes stride over them), then merges the partials j = w,
+// w + WAVES, ... with lane = dimension, so each partial row is one coalesced
+// 256-byte load and WAVES rows are in flight at once; the per-wave sums meet
+// in LDS.
 #include <math.h>
 
 #include "sa_internal.h"
@@ -18,40 +23,69 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-__global__ __launch_bounds__(256) void combine_kernel(const CombineArgs a) {
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+    return x;
+}
+
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a) {
+    __shared__ float s_num[WAVES][64];
+    __shared__ float s_den[WAVES];
     const int lane = threadIdx.x & 63;
-    const int bh = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bh >= a.B * a.Hq) return;
+    const int w = threadIdx.x >> 6;
+    const int bh = blockIdx.x;
     const int h = bh % a.Hq;
     const int S = a.num_splits;
     const float* lse = a.part_lse + (size_t)bh * S;
     const float sig = a.sinks ? a.sinks[h] : -INFINITY;
+
     float M = sig;
-    for (int j = 0; j < S; ++j) M = fmaxf(M, lse[j]);
-    float out = 0.f;
-    if (M != -INFINITY) {
-        float num = 0.f;
-        float den = __builtin_amdgcn_exp2f((sig - M) * kLog2e);
-        const float* po = a.part_o + (size_t)bh * S * kHeadDim + lane;
-#pragma unroll 4
-        for (int j = 0; j < S; ++j) {
-            const float l = lse[j];
-            if (l == -INFINITY) continue;
-            const float w = __builtin_amdgcn_exp2f((l - M) * kLog2e);
-            den += w;
-            num += w * po[(size_t)j * kHeadDim];
-        }
-        out = num / den;
+    for (int j = lane; j < S; j += 64) M = fmaxf(M, lse[j]);
+    M = wave_max(M);
+    if (M == -INFINITY) {                     // nothing attended and no sink
+        if (w == 0) a.out[(size_t)bh * kHeadDim + lane] = 0;
+        return;
     }
-    const __bf16 o = (__bf16)out;
+    float num = 0.f, den = 0.f;
+    const float* po = a.part_o + (size_t)bh * S * kHeadDim + lane;
+#pragma unroll 8
+    for (int j = w; j < S; j += WAVES) {
+        const float l = lse[j];
+        if (l == -INFINITY) continue;
+        const float wt = __builtin_amdgcn_exp2f((l - M) * kLog2e);
+        den += wt;
+        num += wt * po[(size_t)j * kHeadDim];
+    }
+    if (WAVES > 1) {
+        s_num[w][lane] = num;
+        if (lane == 0) s_den[w] = den;
+        __syncthreads();
+        if (w != 0) return;
+        num = 0.f;
+        den = 0.f;
+#pragma unroll
+        for (int i = 0; i < WAVES; ++i) {
+            num += s_num[i][lane];
+            den += s_den[i];
+        }
+    }
+    den += __builtin_amdgcn_exp2f((sig - M) * kLog2e);
+    const __bf16 o = (__bf16)(num / den);
     a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, o);
 }
 
 }  // namespace
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
-    const unsigned grid = (unsigned)((a.B * a.Hq + 3) / 4);
-    hipLaunchKernelGGL(combine_kernel, dim3(grid), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)a.B * a.Hq);
+    if (a.num_splits <= 8)
+        hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(64), 0, stream, a);
+    else if (a.num_splits <= 64)
+        hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -88,6 +88,26 @@ __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Build-time tuning knobs (defaults are the measured best on MI355X):
+//   SA_PIPE   register sets in the load pipeline (2: one step in flight
+//             while the previous one computes);
+//   SA_KV_NT  1: K/V loads carry the non-temporal hint (read-once data).
+#ifndef SA_PIPE
+#define SA_PIPE 2
+#endif
+#ifndef SA_KV_NT
+#define SA_KV_NT 0
+#endif
+constexpr int kPipe = SA_PIPE;
+
+__device__ __forceinline__ u32x4_t load16(const char* p) {
+#if SA_KV_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#else
+    return *reinterpret_cast<const u32x4_t*>(p);
+#endif
+}
+
 struct StepRegs {
     u32x4_t k[4];   // [m*2 + kstep]
     u32x4_t v[4];   // dim tile j
@@ -165,13 +185,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         const char* kp = kbase + (size_t)kblk * blk_stride +
                          ((unsigned)(kc & (bs - 1)) * kHeadDim * 2 + k_lane);
         const char* vp = vbase + (size_t)vblk * blk_stride + ((unsigned)(vc & (bs - 1)) * 2 + v_lane);
-        r.k[0] = *reinterpret_cast<const u32x4_t*>(kp);
-        r.k[1] = *reinterpret_cast<const u32x4_t*>(kp + 64);
-        r.k[2] = *reinterpret_cast<const u32x4_t*>(kp + 4 * kHeadDim * 2);
-        r.k[3] = *reinterpret_cast<const u32x4_t*>(kp + 4 * kHeadDim * 2 + 64);
+        r.k[0] = load16(kp);
+        r.k[1] = load16(kp + 64);
+        r.k[2] = load16(kp + 4 * kHeadDim * 2);
+        r.k[3] = load16(kp + 4 * kHeadDim * 2 + 64);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            r.v[j] = *reinterpret_cast<const u32x4_t*>(vp + (size_t)j * 16 * bs * 2);
+        for (int j = 0; j < 4; ++j) r.v[j] = load16(vp + (size_t)j * 16 * bs * 2);
     };
 
     f32x4_t acc[4];
@@ -229,19 +248,24 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         m_run = m_new;
     };
 
-    // Ping-pong over two register sets: the loads of step s+1 are in flight
-    // while step s computes.  Steps go in pairs; when the count is odd the
-    // extra step is wholly masked (alpha = 1, p = 0), and prefetches past the
-    // last step re-read it (a cache hit), so the loop body has no branch.
+    // Software pipeline over kPipe register sets: while step s computes, the
+    // loads of the next kPipe-1 steps are in flight.  Steps go in groups of
+    // kPipe; steps past the end are wholly masked (alpha = 1, p = 0) and
+    // prefetches past the last step re-read it (a cache hit), so the loop
+    // body has no branch around a load.
     const int nsteps = (t1 - t0 + kStepTokens - 1) / kStepTokens;
     const int last = nsteps - 1;
-    StepRegs A, B;
-    load_step(0, A);
-    for (int s = 0; s < nsteps; s += 2) {
-        load_step(min(s + 1, last), B);
-        compute_step(s, A);
-        load_step(min(s + 2, last), A);
-        compute_step(s + 1, B);
+    StepRegs R[kPipe];
+#pragma unroll
+    for (int i = 0; i < kPipe - 1; ++i) load_step(min(i, last), R[i]);
+    for (int s = 0; s < nsteps; s += kPipe) {
+#pragma unroll
+        for (int i = 0; i < kPipe; ++i) {
+            load_step(min(s + i + kPipe - 1, last), R[(i + kPipe - 1) % kPipe]);
+            // keep the prefetch ahead of this step's math in the schedule
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(s + i, R[i]);
+        }
     }
 
     const float l_tot = sum_xor32(sum_xor16(l_run));

@@ -13,11 +13,15 @@ namespace {
 using sa::kHeadDim;
 
 // Fixed split table (no autotuning, so the result of a call never depends on
-// timing): partitions are 32 * 2^k slots, at most kMaxTableSlice blocks and
-// at most kMaxPartTokens slots long, and shrink until every call has about
-// kTargetWaves partition wavefronts (8 per compute unit of an MI355X).
+// timing).  A partition is 32 * 2^k slots, at most kMaxTableSlice blocks and
+// at most kMaxPartTokens slots, and never longer than the context capacity
+// (a 128-slot ring is one partition).  It halves, down to kMinPartTokens,
+// while a call would have fewer than kMinWaves partition wavefronts.  Chosen
+// from measured sweeps on MI355X: long partitions keep the partial traffic
+// and the combine small; batch-1 calls trade some of that for parallelism.
 constexpr int kMaxPartTokens = 1024;
-constexpr long kTargetWaves = 2048;
+constexpr int kMinPartTokens = 256;
+constexpr long kMinWaves = 128;
 // The last partition of a (b, g) merges the partials itself while there are
 // at most this many; beyond it a separate combine launch is used.
 constexpr int kMaxFusedSplits = 32;
@@ -70,7 +74,10 @@ Plan plan(const sa_dims* d, int32_t window) {
     } else {
         const long units = (long)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
         P = pmax;
-        while (P / 2 >= gran && units * ((max_n + P - 1) / P) < kTargetWaves) P /= 2;
+        while (P / 2 >= gran && P / 2 >= max_n) P /= 2;          // one partition covers it
+        while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
+               units * ((max_n + P - 1) / P) < kMinWaves)
+            P /= 2;
     }
     Plan p;
     p.part_tokens = P;
@@ -80,6 +87,13 @@ Plan plan(const sa_dims* d, int32_t window) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace layout.  The completion counters of the fused combine sit at a
+// fixed place, offset 0, in a region nothing else ever writes: every call
+// returns the counters it used to zero, so a workspace zeroed once stays
+// valid for any later call, whatever its dims or split count.
+constexpr int kCounterSlots = 1 << 16;   // (sequence, KV head) pairs a fused call may have
+constexpr size_t kCounterBytes = (size_t)kCounterSlots * sizeof(int32_t);
+
 struct WorkspaceLayout {
     size_t part_o, part_lse, counters, total;
 };
@@ -88,10 +102,10 @@ WorkspaceLayout workspace_layout(const sa_dims* d, int32_t splits) {
     WorkspaceLayout w{};
     if (splits <= 1) return w;
     const size_t bh = (size_t)d->num_seqs * d->num_q_heads;
-    w.part_o = 0;
-    w.part_lse = align256(bh * splits * kHeadDim * sizeof(float));
-    w.counters = w.part_lse + align256(bh * splits * sizeof(float));
-    w.total = w.counters + align256((size_t)d->num_seqs * d->num_kv_heads * sizeof(int32_t));
+    w.counters = 0;
+    w.part_o = kCounterBytes;
+    w.part_lse = w.part_o + align256(bh * splits * kHeadDim * sizeof(float));
+    w.total = w.part_lse + align256(bh * splits * sizeof(float));
     return w;
 }
 
@@ -190,9 +204,10 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     a.part_o = (float*)(ws + wl.part_o);
     a.part_lse = (float*)(ws + wl.part_lse);
     a.counters = (int32_t*)(ws + wl.counters);
-    const bool fused = dims->variant == SA_VARIANT_MFMA_FUSED ||
-                       (dims->variant == SA_VARIANT_DEFAULT && kFuseByDefault &&
-                        p.splits <= kMaxFusedSplits);
+    const bool fits = (long long)dims->num_seqs * dims->num_kv_heads <= kCounterSlots;
+    const bool fused = fits && (dims->variant == SA_VARIANT_MFMA_FUSED ||
+                                (dims->variant == SA_VARIANT_DEFAULT && kFuseByDefault &&
+                                 p.splits <= kMaxFusedSplits));
     if (fused) {
         a.mode = sa::kFusedCombine;
         return to_status(sa::launch_decode_mfma(a, s));

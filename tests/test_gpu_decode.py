@@ -108,7 +108,10 @@ def test_no_sinks_is_plain_softmax(lib):
 def test_large_sinks_and_scores(lib):
     """Sinks far above and below the scores, and large-magnitude queries."""
     layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
-                             lens=[50, 900, 4000], seed=710, device="cuda", scale=3.0)
+                             lens=[50, 900, 4000], seed=710, device="cuda")
+    # scores with a spread of ~N(0, 9) (q times 4, exact in bf16); V stays
+    # N(0,1) so the output magnitude is the one the tolerance is stated for
+    layer.q.mul_(4.0)
     layer.sinks = torch.tensor([60.0, -60.0, 0.0, 5.0] * 4, device="cuda")
     ref = oracle_attention(layer)
     for v in VARIANTS:
