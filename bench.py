@@ -37,8 +37,11 @@ sys.path.insert(0, _ROOT)
 
 PEAK_HBM = 8.0e12            # MI355X HBM3E, bytes/s
 METRIC = "decode-attn µs/call + achieved HBM GB/s (% of peak), batch 64, 8k ctx"
-KERNEL_SRC = os.path.join(_ROOT, "paged_gqa_decode_step_amd", "csrc", "decode_mfma.hip")
-TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "decode_mfma_batch64_ragged_traffic.json")
+# sources of the dominant call's kernels; the committed counter summary is
+# valid only for the exact sources it was taken on
+KERNEL_SRCS = [os.path.join(_ROOT, "paged_gqa_decode_step_amd", "csrc", f)
+               for f in ("decode_stream.hip", "mfma_attend.h")]
+TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "decode_attention_batch64_ragged_traffic.json")
 
 
 def attn_bytes(lens, window, q_heads=64, kv_heads=8, head_dim=64):
@@ -53,8 +56,11 @@ def append_bytes(batch, kv_heads=8, head_dim=64):
 
 
 def source_digest():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def load_traffic():
@@ -126,6 +132,9 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES, three times, and exit: the "
+                         "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the decode step is built and measured on a "
@@ -133,6 +142,14 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        x = torch.ones(args.copy_calibration // 2, dtype=torch.bfloat16, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(f"# copied {args.copy_calibration} bytes 3 times", flush=True)
+        return
     import paged_gqa_decode_step_amd as sa
     sa.load()
     dev = torch.device("cuda:0")
@@ -147,115 +164,97 @@ def main():
                             variant=args.variant) for L in layers]
     with_append = args.workload == "batch64_ragged"
 
-    def step(evs=None):
-        i = 0
+    def calls_of_step():
+        """The step's calls in order, as (name, bytes, thunk)."""
+        out = []
         for L, o, ws in zip(layers, outs, wss):
+            lens = L.seq_lens.cpu().tolist()
             if with_append:
-                if evs is not None:
-                    evs[i].record(stream)
-                i += 1
-                sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
-                             L.seq_lens, L.window, stream=stream)
-            if evs is not None:
-                evs[i].record(stream)
-            i += 1
-            sa.decode_attention(L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens,
-                                L.sinks, L.window, out=o, workspace=ws,
-                                variant=args.variant, stream=stream)
-        if evs is not None:
-            evs[i].record(stream)
+                out.append((f"append(w={L.window})", append_bytes(L.batch),
+                            lambda L=L: sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache,
+                                                     L.block_table, L.seq_lens, L.window,
+                                                     stream=stream)))
+            out.append((f"attention(w={L.window})",
+                        attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim),
+                        lambda L=L, o=o, ws=ws: sa.decode_attention(
+                            L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
+                            L.window, out=o, workspace=ws, variant=args.variant,
+                            stream=stream)))
+        return out
 
-    ncalls = len(layers) * (2 if with_append else 1)
+    calls = calls_of_step()
+
+    def step():
+        for _, _, f in calls:
+            f()
+
+    def timed(fn, reps):
+        """Mean microseconds of fn over reps back-to-back runs on the stream,
+        bracketed by two HIP events (none in between, so no event gap)."""
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
     print(f"# workload {args.workload}: splits {splits}, warmup {args.warmup}", flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(ncalls + 1)]
-           for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        step(evs[k])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    per_call = [[evs[k][i].elapsed_time(evs[k][i + 1]) * 1e3 for k in range(args.steps)]
-                for i in range(ncalls)]                              # microseconds
-
-    # algorithmic bytes
-    call_bytes, names = [], []
-    for L in layers:
-        lens = L.seq_lens.cpu().tolist()
-        if with_append:
-            call_bytes.append(append_bytes(L.batch))
-            names.append(f"append(w={L.window})")
-        call_bytes.append(attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim))
-        names.append(f"attention(w={L.window})")
-    step_bytes = sum(call_bytes)
+    # the timed region: exactly K steps, events at its two ends only
+    ms_per_step = timed(step, args.steps) / 1e3
+    step_bytes = sum(b for _, b, _ in calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    calls = []
-    for nm, b, us in zip(names, call_bytes, per_call):
-        med = statistics.median(us)
-        calls.append(dict(call=nm, us_median=round(med, 2), us_mean=round(statistics.mean(us), 2),
-                          us_p10=round(sorted(us)[len(us) // 10], 2),
-                          us_p90=round(sorted(us)[(9 * len(us)) // 10], 2),
-                          bytes=b, gbps=round(b / (med * 1e-6) / 1e9, 1),
-                          frac_of_peak=round(b / (med * 1e-6) / PEAK_HBM, 4)))
-        print(f"# {nm}: {med:.2f} us, {b / (med * 1e-6) / 1e9:.1f} GB/s", flush=True)
+    # per-call means: each call alone, K times back to back
+    per_call = []
+    for nm, b, f in calls:
+        us = timed(f, args.steps)
+        per_call.append(dict(call=nm, us_mean=round(us, 2), bytes=b,
+                             gbps=round(b / (us * 1e-6) / 1e9, 1),
+                             frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4)))
+        print(f"# {nm}: {us:.2f} us, {b / (us * 1e-6) / 1e9:.1f} GB/s", flush=True)
 
-    # dominant kernel: the first (full-layer) attention call
+    # dominant kernel: the full-layer attention call
     dom = 1 if with_append else 0
-    dom_us = statistics.mean(per_call[dom])
-    achieved = call_bytes[dom] / (dom_us * 1e-6) / 1e9
+    dom_us = per_call[dom]["us_mean"]
+    achieved = calls[dom][1] / (dom_us * 1e-6) / 1e9
     traffic = load_traffic() if args.workload == "batch64_ragged" and args.variant == 0 else None
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
                     frac=round(achieved * 1e9 / PEAK_HBM, 4), traffic=traffic,
-                    kernel="decode_mfma_kernel", algorithmic_bytes_per_launch=call_bytes[dom],
-                    avg_launch_us=round(dom_us, 2))
+                    kernel=("decode_stream_kernel + combine_stream_kernel (one attention call)"
+                            if splits[0] > 1 and args.variant in (0, 4) else
+                            "decode_mfma_kernel (+ combine_kernel when split)"),
+                    algorithmic_bytes_per_launch=calls[dom][1], avg_launch_us=round(dom_us, 2))
 
     # headline: the attention call alone at batch 64 x 8192
     headline = None
     if args.workload == "batch64_ragged":
-        del layers, outs, wss
-        torch.cuda.empty_cache()
         H = make_workload("batch64_8k", dev)[0]
         ho = torch.empty_like(H.q)
         hws = sa.new_workspace(H.q, H.k_cache, H.v_cache, H.block_table, 0, variant=args.variant)
         for _ in range(args.warmup):
             sa.decode_attention(H.q, H.k_cache, H.v_cache, H.block_table, H.seq_lens, H.sinks, 0,
                                 out=ho, workspace=hws, variant=args.variant, stream=stream)
-        hev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-        torch.cuda.synchronize()
-        for k in range(args.steps):
-            hev[k].record(stream)
-            sa.decode_attention(H.q, H.k_cache, H.v_cache, H.block_table, H.seq_lens, H.sinks, 0,
-                                out=ho, workspace=hws, variant=args.variant, stream=stream)
-        hev[args.steps].record(stream)
-        torch.cuda.synchronize()
-        hus = [hev[k].elapsed_time(hev[k + 1]) * 1e3 for k in range(args.steps)]
+        hmean = timed(lambda: sa.decode_attention(
+            H.q, H.k_cache, H.v_cache, H.block_table, H.seq_lens, H.sinks, 0, out=ho,
+            workspace=hws, variant=args.variant, stream=stream), args.steps)
         hb = attn_bytes([8192] * 64, 0)
-        hmed = statistics.median(hus)
         headline = dict(workload="batch 64 x 8192 tokens, 64/8 heads, D 64, paged bs 16",
-                        us_median=round(hmed, 2), us_p10=round(sorted(hus)[len(hus) // 10], 2),
-                        us_p90=round(sorted(hus)[(9 * len(hus)) // 10], 2), bytes=hb,
-                        gbps=round(hb / (hmed * 1e-6) / 1e9, 1),
-                        frac_of_peak=round(hb / (hmed * 1e-6) / PEAK_HBM, 4),
-                        splits=sa.num_splits(H.q, H.k_cache, H.v_cache, H.block_table, 0,
-                                             variant=args.variant))
-        print(f"# headline batch64x8k: {hmed:.2f} us, {headline['gbps']} GB/s", flush=True)
+                        us_mean=round(hmean, 2), bytes=hb,
+                        gbps=round(hb / (hmean * 1e-6) / 1e9, 1),
+                        frac_of_peak=round(hb / (hmean * 1e-6) / PEAK_HBM, 4))
+        print(f"# headline batch64x8k: {hmean:.2f} us, {headline['gbps']} GB/s", flush=True)
         del H, ho, hws
         torch.cuda.empty_cache()
-        layers = make_workload(args.workload, dev) if not args.no_cpu_baseline else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        if layers is None:
-            layers = make_workload(args.workload, dev)
         print("# timing the oracle on the host...", flush=True)
         sec, npver = time_oracle(layers, args.oracle_reps)
         cpu = dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
@@ -269,7 +268,7 @@ def main():
                config=dict(workload=args.workload, batch=64, q_heads=64, kv_heads=8, head_dim=64,
                            block_size=16, splits=splits, variant=args.variant,
                            step="append+attention per layer" if with_append else "attention"),
-               us_per_call=calls, step_bytes=step_bytes,
+               us_per_call=per_call, step_bytes=step_bytes,
                frac_of_peak=round(value * 1e9 / PEAK_HBM, 4),
                roofline=roofline, cpu_baseline=cpu, headline_uniform_8k=headline)
     print(json.dumps(res), flush=True)

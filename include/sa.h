@@ -90,7 +90,9 @@ enum {
     SA_VARIANT_DEFAULT = 0,
     SA_VARIANT_MFMA_TWO_PASS = 1, /* MFMA partitions, separate combine launch  */
     SA_VARIANT_MFMA_FUSED = 2,    /* MFMA partitions, combine by the last one  */
-    SA_VARIANT_VALU = 3           /* vector-ALU partitions (no MFMA)           */
+    SA_VARIANT_VALU = 3,          /* vector-ALU partitions (no MFMA)           */
+    SA_VARIANT_MFMA_BALANCED = 4  /* MFMA, equal work per wavefront across the
+                                     batch, merge launch for split units       */
 };
 
 /*

@@ -1,0 +1,349 @@
+// The inner loop of decode attention on MFMA, shared by the partition kernels.
+//
+// What is computed (SimpleLLM README, optimisation table: one decode-attention
+// kernel for sinks, sliding window and GQA over the paged cache / ring
+// buffer; tutorial setup page, PagedAttention and FlashAttention chapters):
+// for query head h of KV group g, scores s_p = q_h . K_p / sqrt(D) over a run
+// of slots, an online softmax over them, and sum_p e^(s_p-m) V_p.  The
+// per-head sink logit enters only the final normaliser (no value row), which
+// the callers apply.
+//
+// One 64-lane wavefront serves all G <= 16 query heads of a KV group from one
+// read of each K/V tile: the group's queries form the 16-column operand of
+// v_mfma_f32_16x16x32_bf16, so every K/V byte is read once per group, not
+// once per query head.
+//
+// Per 32-slot step (2 blocks at bs = 16):
+//   S^T[16 slots x 16 heads] = K[16 x 64] Q^T[64 x 16]   two M-tiles, 2 MFMAs each
+//   O^T[64 dims x 16 heads] += V^T[64 x 32] P^T[32 x 16] four MFMAs
+// Operand lanes: lane l = (c16 = l%16, q4 = l/16) supplies row/column c16 and
+// the eight reduction elements of group q4.  The reduction index of both
+// products is a free relabelling, so it is chosen to make every operand a
+// single 16-byte load straight from the cache layout:
+//   * QK^T reduces over dims: lane (c16, q4) holds dims 8*q4..+7 (kstep 0) and
+//     32+8*q4..+7 (kstep 1) of its K row / of its query head;
+//   * M-tile m row r holds slot base + 8*(r/4) + 4*m + r%4, so the S^T output
+//     lane (head c16, q4) ends up with the scores of slots base+8*q4 .. +7;
+//   * PV reduces over slots: that same lane feeds those eight probabilities
+//     as its P^T column, and the V^T operand lane (dim row c16, q4) needs
+//     V[dim][base+8*q4 .. +7], i.e. 16 contiguous bytes of the V^T block.
+// No LDS, no barriers: cross-lane reductions of the softmax max/sum over the
+// four q4 groups use v_permlane16_swap / v_permlane32_swap.
+//
+// Masking: only the last step of a run can reach past its end t1.  Chunks of
+// 8 slots that start at or past t1 are redirected to the chunk holding t1-1
+// (an allocated block) for their loads; their scores become -inf and the V
+// elements of slots >= t1 are zeroed, so stale or NaN data in a block tail
+// can never reach the output.
+#pragma once
+
+#include <math.h>
+
+#include "sa_internal.h"
+
+// Build-time tuning knob (the default is the measured best on MI355X):
+//   SA_KV_NT  1: K/V loads carry the non-temporal hint.  The K/V stream is
+//             read once per call, so keeping it out of the caches leaves them
+//             to the block table, queries and partials (measured +4-7% on
+//             calls that do not fit the 256 MB Infinity Cache).
+#ifndef SA_KV_NT
+#define SA_KV_NT 1
+#endif
+
+namespace sa {
+namespace mfma {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// x[l] op x[l ^ 16] and x[l] op x[l ^ 32] without LDS: each swap gives every
+// lane its own value in one result and its partner's in the other.
+__device__ __forceinline__ float max_xor16(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const unsigned u = __float_as_uint(x);
+    auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+    return __builtin_bit_cast(unsigned, v);
+}
+
+__device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4_t load16(const char* p) {
+#if SA_KV_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+#else
+    return *reinterpret_cast<const u32x4_t*>(p);
+#endif
+}
+
+struct StepRegs {
+    u32x4_t k[4];   // [m*2 + kstep]
+    u32x4_t v[4];   // dim tile j
+};
+
+// Online-softmax state of one wavefront: acc[j] lane (head c16, q4) holds dims
+// 16j + 4*q4 .. +3 of that head; m is the running max (log2 domain, equal on
+// the head's four lanes); l is this lane's share of the running sum.
+struct State {
+    f32x4_t acc[4];
+    float m;
+    float l;
+    __device__ __forceinline__ void reset() {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        l = 0.f;
+    }
+    // sum of l over the head's four lanes
+    __device__ __forceinline__ float total() const { return sum_xor32(sum_xor16(l)); }
+};
+
+// Where one (sequence, KV head) lives, and the lane's fixed offsets.  The
+// block size is a template parameter (bs = 2^BSL) of the functions below so
+// every in-block offset is an immediate of its load.
+struct Unit {
+    const char* kbase;       // K pool + g * (bs*D*2)
+    const char* vbase;       // V pool + g * (bs*D*2)
+    const int32_t* bt_row;   // block table row of the sequence
+    unsigned blk_stride;     // bytes per block across all KV heads
+    unsigned k_lane;         // (c16 & 3) rows + 8*q4 dims, bytes
+    unsigned v_lane;         // c16 dim rows, bytes
+    int bs_log2;
+    int num_blocks;
+    int c16, q4;
+    float scale_log2;
+};
+
+__device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int lane) {
+    Unit u;
+    const int bs = 1 << a.bs_log2;
+    u.c16 = lane & 15;
+    u.q4 = lane >> 4;
+    u.bs_log2 = a.bs_log2;    // == BSL of the kernel instantiation
+    u.num_blocks = a.num_blocks;
+    u.blk_stride = (unsigned)(a.Hkv * bs * kHeadDim * 2);
+    u.kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * bs * kHeadDim * 2;
+    u.vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * bs * kHeadDim * 2;
+    u.bt_row = a.block_table + (size_t)b * a.mbs;
+    u.k_lane = (unsigned)((u.c16 & 3) * kHeadDim + 8 * u.q4) * 2;
+    u.v_lane = (unsigned)(u.c16 * bs) * 2;
+    u.scale_log2 = a.scale_log2;
+    return u;
+}
+
+// Query operand of head g*G + c16 (zero for c16 >= G): dims 8*q4..+7 and
+// 32+8*q4..+7.
+__device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, int lane,
+                                           u32x4_t& qop0, u32x4_t& qop1) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    qop0 = u32x4_t{0u, 0u, 0u, 0u};
+    qop1 = u32x4_t{0u, 0u, 0u, 0u};
+    if (c16 < a.G) {
+        const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * a.G + c16) * kHeadDim + 8 * q4;
+        qop0 = *reinterpret_cast<const u32x4_t*>(qp);
+        qop1 = *reinterpret_cast<const u32x4_t*>(qp + 32);
+    }
+}
+
+// Attend over slots [t0, t1) of one unit (t0 a multiple of 32, t1 > t0, and
+// the run spanning at most kMaxTableSlice blocks), folding into st.
+template <int BSL>
+__device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_t qop0,
+                                           u32x4_t qop1, State& st) {
+    const int c16 = u.c16, q4 = u.q4;
+    constexpr int bs = 1 << BSL;
+    // block-table slice of this run, one entry per lane
+    const int blk0 = t0 >> BSL;
+    const int nblk = ((t1 - 1) >> BSL) - blk0 + 1;
+    int tbl = 0;
+    if (c16 + 16 * q4 < nblk) {
+        tbl = u.bt_row[blk0 + c16 + 16 * q4];
+        tbl = min(max(tbl, 0), u.num_blocks - 1);
+    }
+    const int last_chunk = (t1 - 1) & ~7;
+    const int nsteps = (t1 - t0 + kStepTokens - 1) / kStepTokens;
+
+    // the 8 loads of step s (K: 2 M-tiles x 2 k-steps; V: 4 dim tiles)
+    auto load_step = [&](int s, StepRegs& r) {
+        const int base = t0 + (s << 5);
+        int kc = base + ((c16 >> 2) << 3);           // 8-slot chunk of this lane's K rows
+        int vc = base + (q4 << 3);                   // 8-slot chunk of this lane's V^T run
+        kc = kc < t1 ? kc : last_chunk;
+        vc = vc < t1 ? vc : last_chunk;
+        const unsigned kblk =
+            (unsigned)__builtin_amdgcn_ds_bpermute(((kc >> BSL) - blk0) << 2, tbl);
+        const unsigned vblk =
+            (unsigned)__builtin_amdgcn_ds_bpermute(((vc >> BSL) - blk0) << 2, tbl);
+        const char* kp = u.kbase + (size_t)kblk * u.blk_stride +
+                         ((unsigned)(kc & (bs - 1)) * kHeadDim * 2 + u.k_lane);
+        const char* vp = u.vbase + (size_t)vblk * u.blk_stride +
+                         ((unsigned)(vc & (bs - 1)) * 2 + u.v_lane);
+        r.k[0] = load16(kp);
+        r.k[1] = load16(kp + 64);
+        r.k[2] = load16(kp + 4 * kHeadDim * 2);
+        r.k[3] = load16(kp + 4 * kHeadDim * 2 + 64);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.v[j] = load16(vp + (size_t)j * 16 * bs * 2);
+    };
+
+    auto compute_step = [&](int s, StepRegs& r) {
+        f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        s0 = mfma(r.k[0], qop0, s0);
+        s0 = mfma(r.k[1], qop1, s0);
+        s1 = mfma(r.k[2], qop0, s1);
+        s1 = mfma(r.k[3], qop1, s1);
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[i] = s0[i] * u.scale_log2;
+            t[4 + i] = s1[i] * u.scale_log2;
+        }
+        const int tok = t0 + (s << 5) + (q4 << 3);   // slot of t[0] on this lane
+        if (tok + 8 > t1) {                           // only in a run's last step
+            const int valid = max(0, min(8, t1 - tok));
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (e >= valid) t[e] = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const unsigned mask = (2 * w < valid ? 0x0000FFFFu : 0u) |
+                                      (2 * w + 1 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) r.v[j][w] &= mask;
+            }
+        }
+        float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
+                         fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+        mx = max_xor32(max_xor16(mx));
+        // finite whenever this step or an earlier one of the state had a live
+        // slot; a wholly masked step on a fresh state keeps m = -inf and must
+        // not rescale (exp2(-inf - -inf) would be NaN)
+        const float m_new = fmaxf(st.m, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
+        float p[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(t[e] - m_ref);
+            psum += p[e];
+        }
+        st.l = st.l * alpha + psum;
+        const u32x4_t pop = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
+                             pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            st.acc[j] *= alpha;
+            st.acc[j] = mfma(r.v[j], pop, st.acc[j]);
+        }
+        st.m = m_new;
+    };
+
+    // Two register sets in ping-pong: the loads of step s+1 are in flight
+    // while step s computes.  The loop covers whole pairs that still have a
+    // next step to prefetch; the last one or two steps are peeled, so no load
+    // ever reaches past the run and no load sits under a branch inside the
+    // loop (a conditional load there would make the compiler wait for every
+    // outstanding load at the join).
+    StepRegs A, B;
+    load_step(0, A);
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+        load_step(s + 1, B);
+        __builtin_amdgcn_sched_barrier(0);    // keep the prefetch ahead of the math
+        compute_step(s, A);
+        load_step(s + 2, A);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(s + 1, B);
+    }
+    if (s + 1 < nsteps) {
+        load_step(s + 1, B);
+        __builtin_amdgcn_sched_barrier(0);
+        compute_step(s, A);
+        compute_step(s + 1, B);
+    } else {
+        compute_step(s, A);
+    }
+}
+
+// Attend over slots [t0, t1) of one unit in runs of at most kMaxTableSlice
+// blocks (t0 a multiple of 32).
+template <int BSL>
+__device__ __forceinline__ void attend(const Unit& u, int t0, int t1, u32x4_t qop0,
+                                       u32x4_t qop1, State& st) {
+    constexpr int run = kMaxTableSlice << BSL;
+    for (int r0 = t0; r0 < t1; r0 += run)
+        attend_run<BSL>(u, r0, min(t1, r0 + run), qop0, qop1, st);
+}
+
+// bf16 output of the unit's heads with the sink in the denominator:
+// out = acc / (l + e^(sigma - m)) (all in the log2 domain).
+__device__ __forceinline__ void write_out(const DecodeArgs& a, int b, int g, int lane,
+                                          const State& st, float l_tot) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    if (c16 >= a.G) return;
+    const int h = g * a.G + c16;
+    const float sig = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+    const float inv = 1.0f / (l_tot + __builtin_amdgcn_exp2f(sig - st.m));
+    uint16_t* op = a.out + ((size_t)b * a.Hq + h) * kHeadDim + 4 * q4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x2_t o = {pack_bf16(st.acc[j][0] * inv, st.acc[j][1] * inv),
+                           pack_bf16(st.acc[j][2] * inv, st.acc[j][3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + 16 * j) = o;
+    }
+}
+
+// zeros for the unit's heads (nothing attended: the sink has no value row)
+__device__ __forceinline__ void write_zero(const DecodeArgs& a, int b, int g, int lane) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    if (c16 >= a.G) return;
+    uint16_t* op = a.out + ((size_t)b * a.Hq + g * a.G + c16) * kHeadDim + 4 * q4;
+    const u32x2_t z = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2_t*>(op + 16 * j) = z;
+}
+
+// Partial of a run: o = acc / l (fp32, row of 64 per head at po + head*64),
+// lse = ln sum e^s = (m + log2 l) ln 2 at pl[head].
+__device__ __forceinline__ void write_partial(int G, int lane, const State& st, float l_tot,
+                                              float* po, size_t head_stride, float* pl,
+                                              size_t lse_stride) {
+    const int c16 = lane & 15, q4 = lane >> 4;
+    if (c16 >= G) return;
+    const float inv = 1.0f / l_tot;
+    float* p = po + c16 * head_stride + 4 * q4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t*>(p + 16 * j) = st.acc[j] * inv;
+    if (q4 == 0) pl[c16 * lse_stride] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+}
+
+}  // namespace mfma
+}  // namespace sa

@@ -22,11 +22,22 @@ using sa::kHeadDim;
 constexpr int kMaxPartTokens = 1024;
 constexpr int kMinPartTokens = 256;
 constexpr long kMinWaves = 128;
-// The last partition of a (b, g) merges the partials itself while there are
-// at most this many; beyond it a separate combine launch is used.
-constexpr int kMaxFusedSplits = 32;
-// Whether the default variant fuses the combine (when kMaxFusedSplits allows).
-constexpr bool kFuseByDefault = false;
+// The fused mode (the last partition of a (b, g) merges the partials) is
+// never the default: measured on MI355X, the device-scope fence every
+// partition then needs costs more than the separate combine launch.
+// Balanced kernel: at most kStreamWaves wavefronts (8 per compute unit of an
+// MI355X; measured better than one full round of 12: fewer, longer streams
+// and fewer partials), at most kMaxSegsPerUnit per (sequence, KV head) so a
+// few long units do not turn into hundreds of partials each, and at least
+// kMinStreamSteps 32-slot steps of work each, for batches of up to
+// kMaxStreamSeqs sequences (its per-sequence table lives in LDS).
+#ifndef SA_STREAM_WAVES
+#define SA_STREAM_WAVES 2048
+#endif
+constexpr long kStreamWaves = SA_STREAM_WAVES;
+constexpr long kMaxSegsPerUnit = 128;
+constexpr long kMinStreamSteps = 8;
+constexpr int kMaxStreamSeqs = 2048;
 
 int log2_exact(int x) {
     int l = 0;
@@ -45,7 +56,8 @@ int check_dims(const sa_dims* d, int32_t window) {
     if (d->num_q_heads / d->num_kv_heads > sa::kMaxGroup) return SA_ERR_UNSUPPORTED;
     const int l = log2_exact(d->block_size);
     if (l < 3 || l > 6) return SA_ERR_UNSUPPORTED;
-    if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_VALU) return SA_ERR_INVALID_ARG;
+    if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_MFMA_BALANCED)
+        return SA_ERR_INVALID_ARG;
     if (window > 0 && (window + d->block_size - 1) / d->block_size > d->max_blocks_per_seq)
         return SA_ERR_INVALID_ARG;
     if ((long long)d->num_blocks * d->num_kv_heads * d->block_size * kHeadDim > (1LL << 40))
@@ -95,17 +107,61 @@ constexpr int kCounterSlots = 1 << 16;   // (sequence, KV head) pairs a fused ca
 constexpr size_t kCounterBytes = (size_t)kCounterSlots * sizeof(int32_t);
 
 struct WorkspaceLayout {
-    size_t part_o, part_lse, counters, total;
+    size_t part_o, part_lse, counters, plan, total;
 };
 
-WorkspaceLayout workspace_layout(const sa_dims* d, int32_t splits) {
+enum class Mode { kStatic, kFused, kBalanced };
+
+// Wavefronts of the balanced kernel for these dims (an upper bound on the
+// work is all the host knows: the lengths live on the device).
+long stream_waves(const sa_dims* d, int32_t window) {
+    const long cap = (long)d->max_blocks_per_seq * d->block_size;
+    const long max_n = window > 0 ? (window < cap ? window : cap) : cap;
+    const long t_upper = (long)d->num_seqs * d->num_kv_heads *
+                         ((max_n + sa::kStepTokens - 1) / sa::kStepTokens);
+    long nw = (t_upper + kMinStreamSteps - 1) / kMinStreamSteps;
+    const long seg_cap = (long)d->num_seqs * d->num_kv_heads * kMaxSegsPerUnit;
+    if (nw > seg_cap) nw = seg_cap;
+    return nw < 1 ? 1 : (nw > kStreamWaves ? kStreamWaves : nw);
+}
+
+// Which kernel a call with these dims uses (assumes check_dims passed).
+Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
+    const bool fits_stream = d->num_seqs <= kMaxStreamSeqs;
+    switch (d->variant) {
+        case SA_VARIANT_MFMA_BALANCED:
+            return fits_stream ? Mode::kBalanced : Mode::kStatic;
+        case SA_VARIANT_MFMA_FUSED:
+            return (long long)d->num_seqs * d->num_kv_heads <= kCounterSlots ? Mode::kFused
+                                                                             : Mode::kStatic;
+        case SA_VARIANT_MFMA_TWO_PASS:
+            return Mode::kStatic;
+        default:
+            // one static partition needs no merge at all; beyond that the
+            // balanced kernel keeps every compute unit equally busy
+            if (d->num_splits > 0 || p.splits == 1 || !fits_stream) return Mode::kStatic;
+            return Mode::kBalanced;
+    }
+}
+
+WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p, Mode m) {
     WorkspaceLayout w{};
-    if (splits <= 1) return w;
-    const size_t bh = (size_t)d->num_seqs * d->num_q_heads;
+    size_t rows, lse;        // partial rows of D floats, and lse entries
+    if (m == Mode::kBalanced) {
+        const size_t slots = (size_t)stream_waves(d, window) * 2 *
+                             (d->num_q_heads / d->num_kv_heads);
+        rows = slots;
+        lse = slots;
+    } else {
+        if (p.splits <= 1) return w;
+        rows = (size_t)d->num_seqs * d->num_q_heads * p.splits;
+        lse = rows;
+    }
     w.counters = 0;
     w.part_o = kCounterBytes;
-    w.part_lse = w.part_o + align256(bh * splits * kHeadDim * sizeof(float));
-    w.total = w.part_lse + align256(bh * splits * sizeof(float));
+    w.part_lse = w.part_o + align256(rows * kHeadDim * sizeof(float));
+    w.plan = w.part_lse + align256(lse * sizeof(float));
+    w.total = w.plan + align256((size_t)d->num_seqs * sizeof(int32_t));
     return w;
 }
 
@@ -168,7 +224,8 @@ int32_t sa_decode_num_splits(const sa_dims* dims, int32_t window) {
 
 size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window) {
     if (check_dims(dims, window) != SA_OK) return 0;
-    return workspace_layout(dims, plan(dims, window).splits).total;
+    const Plan p = plan(dims, window);
+    return workspace_layout(dims, window, p, choose_mode(dims, window, p)).total;
 }
 
 int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
@@ -184,7 +241,8 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     if (dims->variant == SA_VARIANT_VALU) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
-    const WorkspaceLayout wl = workspace_layout(dims, p.splits);
+    const Mode mode = choose_mode(dims, window, p);
+    const WorkspaceLayout wl = workspace_layout(dims, window, p, mode);
     if (wl.total && (!workspace || workspace_bytes < wl.total)) return SA_ERR_WORKSPACE;
 
     sa::DecodeArgs a = decode_args(dims, window, p);
@@ -196,19 +254,22 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     a.sinks = sinks;
     a.out = out;
     hipStream_t s = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    if (mode == Mode::kBalanced) {
+        a.part_o = (float*)(ws + wl.part_o);
+        a.part_lse = (float*)(ws + wl.part_lse);
+        a.plan = (int32_t*)(ws + wl.plan);
+        a.num_waves = (int32_t)stream_waves(dims, window);
+        return to_status(sa::launch_decode_stream(a, s));
+    }
     if (p.splits == 1) {
         a.mode = sa::kWriteOut;
         return to_status(sa::launch_decode_mfma(a, s));
     }
-    char* ws = (char*)workspace;
     a.part_o = (float*)(ws + wl.part_o);
     a.part_lse = (float*)(ws + wl.part_lse);
     a.counters = (int32_t*)(ws + wl.counters);
-    const bool fits = (long long)dims->num_seqs * dims->num_kv_heads <= kCounterSlots;
-    const bool fused = fits && (dims->variant == SA_VARIANT_MFMA_FUSED ||
-                                (dims->variant == SA_VARIANT_DEFAULT && kFuseByDefault &&
-                                 p.splits <= kMaxFusedSplits));
-    if (fused) {
+    if (mode == Mode::kFused) {
         a.mode = sa::kFusedCombine;
         return to_status(sa::launch_decode_mfma(a, s));
     }

@@ -39,6 +39,8 @@ struct DecodeArgs {
     float* part_o;            // kWritePartials, kFusedCombine
     float* part_lse;
     int32_t* counters;        // kFusedCombine: [B*Hkv], zero between calls
+    int32_t* plan;            // balanced kernel: [B] step prefix, for its combine
+    int32_t num_waves;        // balanced kernel: wavefronts in the grid
     int32_t B, Hq, Hkv, G;
     int32_t bs_log2, mbs, num_blocks, window;
     int32_t num_splits;       // S
@@ -57,6 +59,7 @@ struct CombineArgs {
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -14,7 +14,7 @@ from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tai
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [0, 1, 2]
+VARIANTS = [0, 1, 2, 4]     # default, static two-pass, static fused, balanced
 
 
 def attend(lib, layer, num_splits=0, variant=0, sinks="layer"):
@@ -248,3 +248,20 @@ def test_workspace_reused_across_calls(lib):
                                        num_splits=S, variant=2)
             torch.cuda.synchronize()
             assert_parity(out_f64(out), ref, f"reuse {i} S={S}")
+
+
+@pytest.mark.parametrize("W", [0, 128])
+@pytest.mark.parametrize("B,lo,hi", [(5, 0, 3000), (37, 0, 700), (200, 1, 2500), (1, 9000, 9000)])
+def test_balanced_kernel_edge_cases(lib, W, B, lo, hi):
+    """The equal-work kernel over ragged batches with empty sequences, more
+    than 64 sequences (several scan chunks), and a single long sequence whose
+    units spread over many wavefronts."""
+    lens = synth.ragged_lengths(1234 + B, B, lo, hi).tolist()
+    layer = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=lens, window=W, seed=2000 + B + W, device="cuda",
+                             capacity=[max(1, L) for L in lens])
+    ref = oracle_attention(layer)
+    for v in (0, 4):
+        a = attend(lib, layer, variant=v)
+        assert_parity(out_f64(a), ref, f"balanced B={B} W={W} v={v}")
+        assert torch.equal(a, attend(lib, layer, variant=v)), "not deterministic"
