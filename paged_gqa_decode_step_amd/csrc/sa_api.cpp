@@ -135,6 +135,7 @@ Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
             return (long long)d->num_seqs * d->num_kv_heads <= kCounterSlots ? Mode::kFused
                                                                              : Mode::kStatic;
         case SA_VARIANT_MFMA_TWO_PASS:
+        case SA_VARIANT_VALU:
             return Mode::kStatic;
         default:
             // one static partition needs no merge at all; beyond that the
@@ -238,10 +239,12 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     if (dims->num_seqs == 0) return SA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return SA_ERR_INVALID_ARG;
-    if (dims->variant == SA_VARIANT_VALU) return SA_ERR_UNSUPPORTED;
+    const bool valu = dims->variant == SA_VARIANT_VALU;
+    if (valu && dims->num_q_heads / dims->num_kv_heads > 8) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
     const Mode mode = choose_mode(dims, window, p);
+    auto launch_static = valu ? sa::launch_decode_valu : sa::launch_decode_mfma;
     const WorkspaceLayout wl = workspace_layout(dims, window, p, mode);
     if (wl.total && (!workspace || workspace_bytes < wl.total)) return SA_ERR_WORKSPACE;
 
@@ -264,7 +267,7 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     }
     if (p.splits == 1) {
         a.mode = sa::kWriteOut;
-        return to_status(sa::launch_decode_mfma(a, s));
+        return to_status(launch_static(a, s));
     }
     a.part_o = (float*)(ws + wl.part_o);
     a.part_lse = (float*)(ws + wl.part_lse);
@@ -274,7 +277,7 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
         return to_status(sa::launch_decode_mfma(a, s));
     }
     a.mode = sa::kWritePartials;
-    st = to_status(sa::launch_decode_mfma(a, s));
+    st = to_status(launch_static(a, s));
     if (st != SA_OK) return st;
     sa::CombineArgs c{};
     c.part_o = a.part_o;

@@ -14,7 +14,7 @@ from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tai
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [0, 1, 2, 4]     # default, static two-pass, static fused, balanced
+VARIANTS = [0, 1, 2, 3, 4]  # default, static two-pass, static fused, vector-ALU, balanced
 
 
 def attend(lib, layer, num_splits=0, variant=0, sinks="layer"):
