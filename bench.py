@@ -2,31 +2,37 @@
 """Benchmark of the decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch64_ragged]
+                    [--configs all|none] [--graph]
 
-A step is one pass of the whole hot path over one batch: for the default
-workload (batch 64, 64 query / 8 KV heads, D 64, block size 16, ragged
-context 512..8192 plus one appended token) it is the KV append and decode
-attention of a paged full-attention layer, then the KV append and decode
-attention of a sliding-window-128 ring layer.  Inputs are seeded synthetic
-bf16 N(0,1) values, resident in HBM before timing starts.
+A step is one pass of the whole hot path over one batch.  For the default
+workload it is the KV append and decode attention of a paged full-attention
+layer, then the KV append and decode attention of a sliding-window-128 ring
+layer.  The batch is 64 sequences with 64 query / 8 KV heads, D 64, block size
+16, and a ragged context of 512..8192 plus one appended token.  Inputs are
+seeded synthetic bf16 N(0,1) values, resident in HBM before timing starts.
 
-Reported (one JSON line): ``value`` is the step's algorithmic bytes divided by
-its time (GB/s); the algorithmic bytes of an attention call are 2048 B per
-attended token (K and V rows of 8 KV heads x 64 dims x bf16) plus 16 KiB per
-sequence (its bf16 query and output rows), and an append moves 4 KiB per
-sequence (read and write of K and V rows).  ``roofline`` covers the dominant
-kernel (the full-layer attention call), timed with HIP events on the stream
-it runs on.  ``cpu_baseline`` is the fp64 oracle timed on this host on the
-same workload.  ``headline_uniform_8k`` is the attention call alone at batch
-64 x 8192 tokens.
+Reported (one JSON line):
+  value        the step's algorithmic bytes / its time (GB/s).  An attention
+               call moves 2048 B per attended token (K and V rows of 8 KV heads
+               x 64 dims x bf16) plus 16 KiB per sequence (its bf16 query and
+               output rows); an append moves 4 KiB per sequence (read and write
+               of K and V rows).
+  roofline     the dominant call (the full-layer attention), timed with HIP
+               events on the stream it runs on, back to back.
+  cpu_baseline the fp64 oracle on this host, on the same step.
+  configs      every synthetic configuration: GPU us per call, GB/s and
+               fraction of peak, next to the oracle's seconds on a bounded
+               sample of the same inputs (scaled to the whole call).  Calls
+               whose inputs fit the 256 MB Infinity Cache rotate several input
+               sets so every call reads HBM.
 """
 
 from __future__ import annotations
 
 import argparse
+import contextlib
 import hashlib
 import json
-import math
 import os
 import statistics
 import sys
@@ -36,6 +42,7 @@ _ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, _ROOT)
 
 PEAK_HBM = 8.0e12            # MI355X HBM3E, bytes/s
+MALL_BYTES = 256 << 20       # Infinity Cache
 METRIC = "decode-attn µs/call + achieved HBM GB/s (% of peak), batch 64, 8k ctx"
 # sources of the dominant call's kernels; the committed counter summary is
 # valid only for the exact sources it was taken on
@@ -46,9 +53,7 @@ TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "decode_attention_batch64_ragged_
 
 def attn_bytes(lens, window, q_heads=64, kv_heads=8, head_dim=64):
     n = [min(int(L), window) if window > 0 else int(L) for L in lens]
-    per_tok = kv_heads * head_dim * 2 * 2
-    per_seq = q_heads * head_dim * 2 * 2
-    return sum(n) * per_tok + len(lens) * per_seq
+    return sum(n) * kv_heads * head_dim * 2 * 2 + len(lens) * q_heads * head_dim * 2 * 2
 
 
 def append_bytes(batch, kv_heads=8, head_dim=64):
@@ -64,8 +69,8 @@ def source_digest():
 
 
 def load_traffic():
-    """Per-launch HBM bytes of the dominant kernel from the committed counter
-    summary, or None if there is none or the kernel source changed since."""
+    """Per-launch HBM bytes of the dominant call from the committed counter
+    summary, or None if there is none or the kernel sources changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -76,52 +81,279 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
-def make_workload(name, device):
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def ragged_layers(device, seed_offset=0):
+    import synth
+    c = synth.CONFIGS["batch64_ragged"]
+    lens = synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + 1
+    common = dict(batch=c["batch"], q_heads=c["q_heads"], kv_heads=c["kv_heads"],
+                  head_dim=c["head_dim"], block_size=c["block_size"], lens=lens, device=device)
+    return [synth.make_layer(window=0, seed=c["seed"] + 10 + seed_offset, **common),
+            synth.make_layer(window=128, seed=c["seed"] + 20 + seed_offset, **common)]
+
+
+def make_workload(name, device, seed_offset=0):
     import synth
     if name == "batch64_ragged":
-        c = synth.CONFIGS[name]
-        lens = synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + 1
-        common = dict(batch=c["batch"], q_heads=c["q_heads"], kv_heads=c["kv_heads"],
-                      head_dim=c["head_dim"], block_size=c["block_size"], lens=lens,
-                      device=device)
-        return [synth.make_layer(window=0, seed=c["seed"] + 10, **common),
-                synth.make_layer(window=128, seed=c["seed"] + 20, **common)]
-    if name in ("batch64_8k", "gptoss_layer_8k", "long_131k_b1", "long_131k_b8"):
+        return ragged_layers(device, seed_offset)
+    if name in ("tiny", "batch64_8k", "gptoss_layer_8k", "long_131k_b1", "long_131k_b8"):
         c = dict(synth.CONFIGS[name])
+        c["seed"] += seed_offset
         return [synth.make_layer(device=device, **c)]
     raise SystemExit(f"unknown workload {name}")
 
 
-def time_oracle(layers, reps):
-    """Median wall time of the fp64 oracle over the whole step (append and
-    attention of every layer), BLAS held to one thread."""
-    import numpy as np
-    import oracle
-    import synth
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+
+class Timer:
+    """HIP-event timing on one stream.  ``settle`` runs the measured call until
+    it has kept the GPU busy for SETTLE_S seconds: after host-side work the
+    GPU's clocks drop and take that long to return, and a short warmup would
+    time the ramp instead of the steady state."""
+    SETTLE_S = 0.1
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def settle(self, fn, min_reps):
+        done, elapsed_us = 0, 0.0
+        while done < min_reps or elapsed_us < self.SETTLE_S * 1e6:
+            n = max(min_reps, 8)
+            elapsed_us += self.mean_us(fn, n) * n
+            done += n
+
+    def mean_us(self, fn, reps):
+        """Mean microseconds of fn over reps back-to-back runs on the stream,
+        bracketed by two HIP events (none in between, so no event gap)."""
+        torch = self.torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for i in range(reps):
+            fn(i)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+
+@contextlib.contextmanager
+def one_blas_thread():
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:                      # pragma: no cover
-        threadpool_limits = None
-    host = []
-    for L in layers:
-        host.append(dict(q=synth.to_bits(L.q), k=synth.to_bits(L.k_cache),
-                         v=synth.to_bits(L.v_cache), bt=synth.to_bits(L.block_table),
-                         lens=synth.to_bits(L.seq_lens), kn=synth.to_bits(L.k_new),
-                         vn=synth.to_bits(L.v_new),
-                         sinks=None if L.sinks is None else L.sinks.cpu().numpy(),
-                         w=L.window))
-    import contextlib
+        yield
+        return
+    with threadpool_limits(limits=1):
+        yield
+
+
+def host_inputs(layer, seqs=None):
+    """Host copies (bf16 bits) of a layer's inputs; with ``seqs`` only those
+    sequences, their pool blocks and a remapped table."""
+    import numpy as np
+    import synth
+    import torch
+    if seqs is None:
+        return dict(q=synth.to_bits(layer.q), k=synth.to_bits(layer.k_cache),
+                    v=synth.to_bits(layer.v_cache), bt=synth.to_bits(layer.block_table),
+                    lens=synth.to_bits(layer.seq_lens), kn=synth.to_bits(layer.k_new),
+                    vn=synth.to_bits(layer.v_new),
+                    sinks=None if layer.sinks is None else layer.sinks.cpu().numpy(),
+                    w=layer.window)
+    bt = layer.block_table.cpu().numpy()
+    owned = [bt[b, :layer.blocks_per_seq[b]] for b in seqs]
+    ids = np.concatenate(owned + [np.array([layer.poison_block])]).astype(np.int64)
+    idx = torch.as_tensor(ids, device=layer.k_cache.device)
+    new_bt = np.full((len(seqs), bt.shape[1]), len(ids) - 1, dtype=np.int32)
+    start = 0
+    for i, o in enumerate(owned):
+        new_bt[i, :len(o)] = np.arange(start, start + len(o))
+        start += len(o)
+    sel = torch.as_tensor(list(seqs), device=layer.q.device)
+    return dict(q=synth.to_bits(layer.q.index_select(0, sel)),
+                k=synth.to_bits(layer.k_cache.index_select(0, idx)),
+                v=synth.to_bits(layer.v_cache.index_select(0, idx)), bt=new_bt,
+                lens=layer.seq_lens.cpu().numpy()[list(seqs)],
+                kn=synth.to_bits(layer.k_new.index_select(0, sel)),
+                vn=synth.to_bits(layer.v_new.index_select(0, sel)),
+                sinks=None if layer.sinks is None else layer.sinks.cpu().numpy(),
+                w=layer.window)
+
+
+def oracle_seconds(hosts, reps, append=True):
+    """Median wall seconds of the fp64 oracle over the given host inputs
+    (append, when asked, then attention), BLAS held to one thread."""
+    import oracle
     times = []
-    limit = threadpool_limits(limits=1) if threadpool_limits else contextlib.nullcontext()
-    with limit:
+    with one_blas_thread():
         for _ in range(reps):
             t0 = time.perf_counter()
-            for h in host:
-                k, v = oracle.kv_append(h["k"], h["v"], h["kn"], h["vn"], h["bt"], h["lens"], h["w"])
+            for h in hosts:
+                k, v = h["k"], h["v"]
+                if append:
+                    k, v = oracle.kv_append(k, v, h["kn"], h["vn"], h["bt"], h["lens"], h["w"])
                 oracle.decode_attention(h["q"], k, v, h["bt"], h["lens"], h["sinks"], h["w"])
             times.append(time.perf_counter() - t0)
-    return statistics.median(times), np.__version__
+    return statistics.median(times)
 
+
+def entry(name, what, us, nbytes, cpu_s=None, cpu_note=None, **extra):
+    e = dict(config=name, call=what, us=round(us, 2), bytes=int(nbytes),
+             gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+             frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4))
+    if cpu_s is not None:
+        e["oracle_s"] = round(cpu_s, 4)
+        e["oracle_gbps"] = round(nbytes / cpu_s / 1e9, 4)
+        e["oracle_sample"] = cpu_note
+        e["gpu_speedup_vs_oracle"] = round(cpu_s / (us * 1e-6), 1)
+    e.update(extra)
+    return e
+
+
+# ---------------------------------------------------------------------------
+# per-configuration measurements
+# ---------------------------------------------------------------------------
+
+def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
+                     with_oracle=True, oracle_seqs=None, label=None):
+    """One attention call per launch, rotating input sets past the Infinity
+    Cache.  Calls too short for Python to keep the GPU fed (under 40 us) are
+    timed by replaying a HIP graph of many launches.  Returns the entry and,
+    for the oracle timed later, host copies of one input set (or of the given
+    sequences)."""
+    first = make_workload(name, dev)[0]
+    one = attn_bytes(first.seq_lens.cpu().tolist(), first.window, first.q_heads,
+                     first.kv_heads, first.head_dim)
+    pool = first.k_cache.numel() * 4
+    nsets = 1 if pool > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // max(pool, 1)))
+    sets = [first] + [make_workload(name, dev, seed_offset=101 * i)[0] for i in range(1, nsets)]
+    ws = sa.new_workspace(first.q, first.k_cache, first.v_cache, first.block_table,
+                          first.window, variant=variant)
+    outs = [torch.empty_like(L.q) for L in sets]
+
+    def call(i):
+        L = sets[i % len(sets)]
+        sa.decode_attention(L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
+                            L.window, out=outs[i % len(sets)], workspace=ws, variant=variant)
+    timer.settle(call, warmup)
+    us = timer.mean_us(call, steps)
+    timing = "eager, back to back"
+    if us < 40.0:
+        per_graph = max(len(sets), 32)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                call(i)
+        reps = max(2, steps // 10)
+        timer.settle(lambda _: g.replay(), reps)
+        us = timer.mean_us(lambda _: g.replay(), reps) / per_graph
+        timing = f"HIP graph of {per_graph} launches, replayed {reps} times"
+        del g
+    host = note = None
+    if with_oracle:
+        B = first.batch
+        seqs = oracle_seqs if oracle_seqs is not None else list(range(B))
+        host = (host_inputs(first, seqs if len(seqs) < B else None), B / len(seqs),
+                1 if len(seqs) * max(first.seq_lens.cpu().tolist()) > 10 ** 5 else 3)
+        note = (f"{len(seqs)} of {B} sequences, scaled x{B / len(seqs):g}" if len(seqs) < B
+                else "every sequence")
+    e = entry(label or name, "attention", us, one, input_sets=len(sets), timing=timing,
+              splits=sa.num_splits(first.q, first.k_cache, first.v_cache, first.block_table,
+                                   first.window, variant=variant))
+    if note:
+        e["oracle_sample"] = note
+    del sets, outs, ws
+    torch.cuda.empty_cache()
+    return e, host
+
+
+def add_oracle(e, host):
+    """Time the oracle on the saved host inputs and add it to the entry."""
+    h, scale, reps = host
+    cpu_s = oracle_seconds([h], reps, append=False) * scale
+    e["oracle_s"] = round(cpu_s, 4)
+    e["oracle_gbps"] = round(e["bytes"] / cpu_s / 1e9, 4)
+    e["oracle_sample"] += f"; median of {reps}; NumPy fp64, 1 thread"
+    e["gpu_speedup_vs_oracle"] = round(cpu_s / (e["us"] * 1e-6), 1)
+
+
+def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=50,
+                       graph=False, oracle_seqs=(0, 21, 42, 63), with_oracle=True):
+    """The decode loop: 24 layers alternating ring-128 / paged full attention,
+    batch 64, initial lengths 1024..32768, 50 steps each appending one token
+    per sequence in every layer.  Timed as whole steps (all layers), eagerly
+    or replayed from a HIP graph of one step."""
+    import synth
+    c = synth.CONFIGS["decode_loop"]
+    B, W = c["batch"], c["window"]
+    L0 = synth.ragged_lengths(c["seed"], B, *c["len_range"])
+    model = []
+    for li in range(layers):
+        w = W if li % 2 == 0 else 0
+        model.append(synth.make_layer(batch=B, q_heads=64, kv_heads=8, head_dim=64,
+                                      block_size=16, lens=L0 + 1, capacity=L0 + steps,
+                                      window=w, seed=c["seed"] * 100 + li, device=dev))
+    lens = model[0].seq_lens.clone()
+    start_lens = lens.clone()
+    ws_bytes = max(sa.workspace_bytes(m.q, m.k_cache, m.v_cache, m.block_table, m.window,
+                                      variant=variant) for m in model)
+    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    outs = [torch.empty_like(m.q) for m in model]
+
+    def step(_=0):
+        # launches go to torch's current stream: the timed stream when eager,
+        # the capture stream while a HIP graph is being recorded
+        for m, o in zip(model, outs):
+            sa.kv_append(m.k_new, m.v_new, m.k_cache, m.v_cache, m.block_table, lens, m.window)
+            sa.decode_attention(m.q, m.k_cache, m.v_cache, m.block_table, lens, m.sinks,
+                                m.window, out=o, workspace=ws, variant=variant)
+        lens.add_(1)
+
+    # bytes of the timed steps (lengths grow by one each step)
+    total = 0
+    for t in range(steps):
+        cur = (L0 + 1 + t).tolist()
+        for m in model:
+            total += attn_bytes(cur, m.window) + append_bytes(B)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    lens.copy_(start_lens)
+    runner = step
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        torch.cuda.synchronize()
+        lens.copy_(start_lens)
+        runner = lambda _=0: g.replay()                                   # noqa: E731
+    timer.settle(runner, 4)                  # (its appends only rewrite slots of these steps)
+    lens.copy_(start_lens)
+    us_step = timer.mean_us(runner, steps)
+    cpu_step = note = None
+    if with_oracle:
+        lens.copy_(start_lens)
+        for m in model:
+            m.seq_lens.copy_(lens)
+        hosts = [host_inputs(m, list(oracle_seqs)) for m in model]
+        cpu_step = oracle_seconds(hosts, 1) * B / len(oracle_seqs)
+        note = (f"{len(oracle_seqs)} of {B} sequences, all {layers} layers, one step, scaled "
+                f"x{B / len(oracle_seqs):g}; NumPy fp64, 1 thread")
+    e = entry("decode_loop", f"step ({layers} layers: append + attention each)", us_step,
+              total / steps, cpu_step, note, steps=steps, layers=layers,
+              loop_ms=round(us_step * steps / 1e3, 3), hip_graph=graph)
+    del model, outs, ws
+    torch.cuda.empty_cache()
+    return e
+
+
+# ---------------------------------------------------------------------------
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
@@ -132,6 +364,10 @@ def main():
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-reps", type=int, default=3)
+    ap.add_argument("--configs", choices=("all", "none"), default="all",
+                    help="also report every synthetic configuration (default: all)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the decode loop's step from a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, three times, and exit: the "
                          "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -155,6 +391,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
+    timer = Timer(torch, stream)
 
     layers = make_workload(args.workload, dev)
     outs = [torch.empty_like(L.q) for L in layers]
@@ -164,57 +401,37 @@ def main():
                             variant=args.variant) for L in layers]
     with_append = args.workload == "batch64_ragged"
 
-    def calls_of_step():
-        """The step's calls in order, as (name, bytes, thunk)."""
-        out = []
-        for L, o, ws in zip(layers, outs, wss):
-            lens = L.seq_lens.cpu().tolist()
-            if with_append:
-                out.append((f"append(w={L.window})", append_bytes(L.batch),
-                            lambda L=L: sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache,
-                                                     L.block_table, L.seq_lens, L.window,
-                                                     stream=stream)))
-            out.append((f"attention(w={L.window})",
-                        attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim),
-                        lambda L=L, o=o, ws=ws: sa.decode_attention(
-                            L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
-                            L.window, out=o, workspace=ws, variant=args.variant,
-                            stream=stream)))
-        return out
+    calls = []                               # (name, bytes, thunk) in step order
+    for L, o, ws in zip(layers, outs, wss):
+        lens = L.seq_lens.cpu().tolist()
+        if with_append:
+            calls.append((f"append(w={L.window})", append_bytes(L.batch),
+                          lambda _=0, L=L: sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache,
+                                                        L.block_table, L.seq_lens, L.window,
+                                                        stream=stream)))
+        calls.append((f"attention(w={L.window})",
+                       attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim),
+                       lambda _=0, L=L, o=o, ws=ws: sa.decode_attention(
+                           L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
+                           L.window, out=o, workspace=ws, variant=args.variant, stream=stream)))
 
-    calls = calls_of_step()
-
-    def step():
+    def step(_=0):
         for _, _, f in calls:
             f()
 
-    def timed(fn, reps):
-        """Mean microseconds of fn over reps back-to-back runs on the stream,
-        bracketed by two HIP events (none in between, so no event gap)."""
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(reps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
     print(f"# workload {args.workload}: splits {splits}, warmup {args.warmup}", flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    timer.settle(step, args.warmup)
 
     # the timed region: exactly K steps, events at its two ends only
-    ms_per_step = timed(step, args.steps) / 1e3
+    ms_per_step = timer.mean_us(step, args.steps) / 1e3
     step_bytes = sum(b for _, b, _ in calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # per-call means: each call alone, K times back to back
     per_call = []
     for nm, b, f in calls:
-        us = timed(f, args.steps)
+        timer.settle(f, args.warmup)
+        us = timer.mean_us(f, args.steps)
         per_call.append(dict(call=nm, us_mean=round(us, 2), bytes=b,
                              gbps=round(b / (us * 1e-6) / 1e9, 1),
                              frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4)))
@@ -232,35 +449,45 @@ def main():
                             "decode_mfma_kernel (+ combine_kernel when split)"),
                     algorithmic_bytes_per_launch=calls[dom][1], avg_launch_us=round(dom_us, 2))
 
-    # headline: the attention call alone at batch 64 x 8192
+    main_hosts = None if args.no_cpu_baseline else [host_inputs(L) for L in layers]
+    del calls, layers, outs, wss
+    torch.cuda.empty_cache()
+
+    configs = []
     headline = None
-    if args.workload == "batch64_ragged":
-        H = make_workload("batch64_8k", dev)[0]
-        ho = torch.empty_like(H.q)
-        hws = sa.new_workspace(H.q, H.k_cache, H.v_cache, H.block_table, 0, variant=args.variant)
-        for _ in range(args.warmup):
-            sa.decode_attention(H.q, H.k_cache, H.v_cache, H.block_table, H.seq_lens, H.sinks, 0,
-                                out=ho, workspace=hws, variant=args.variant, stream=stream)
-        hmean = timed(lambda: sa.decode_attention(
-            H.q, H.k_cache, H.v_cache, H.block_table, H.seq_lens, H.sinks, 0, out=ho,
-            workspace=hws, variant=args.variant, stream=stream), args.steps)
-        hb = attn_bytes([8192] * 64, 0)
-        headline = dict(workload="batch 64 x 8192 tokens, 64/8 heads, D 64, paged bs 16",
-                        us_mean=round(hmean, 2), bytes=hb,
-                        gbps=round(hb / (hmean * 1e-6) / 1e9, 1),
-                        frac_of_peak=round(hb / (hmean * 1e-6) / PEAK_HBM, 4))
-        print(f"# headline batch64x8k: {hmean:.2f} us, {headline['gbps']} GB/s", flush=True)
-        del H, ho, hws
-        torch.cuda.empty_cache()
+    if args.configs == "all" and args.workload == "batch64_ragged":
+        oc = not args.no_cpu_baseline
+        hosts = []
+        for nm, kw in (("batch64_8k", dict(oracle_seqs=[0, 21, 42, 63],
+                                           label="batch64_8k (headline)")),
+                       ("tiny", {}), ("gptoss_layer_8k", {}), ("long_131k_b1", {}),
+                       ("long_131k_b8", dict(oracle_seqs=[3]))):
+            e, h = attention_config(sa, torch, timer, dev, nm, steps=args.steps,
+                                    warmup=args.warmup, variant=args.variant, with_oracle=oc,
+                                    **kw)
+            configs.append(e)
+            hosts.append(h)
+            print(f"# {e['config']}: {e['us']} us, {e['gbps']} GB/s", flush=True)
+        headline = configs[0]
+        loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
+                                  with_oracle=oc)
+        configs.append(loop)
+        print(f"# decode loop: {loop['us']} us per step, {loop['gbps']} GB/s", flush=True)
+        if oc:                               # host timings after all GPU timings
+            print("# timing the oracle on the configurations...", flush=True)
+            for e, h in zip(configs, hosts):
+                add_oracle(e, h)
 
     cpu = None
-    if not args.no_cpu_baseline:
-        print("# timing the oracle on the host...", flush=True)
-        sec, npver = time_oracle(layers, args.oracle_reps)
+    if main_hosts is not None:
+        print("# timing the oracle on the step...", flush=True)
+        sec = oracle_seconds(main_hosts, args.oracle_reps, append=with_append)
+        import numpy as np
         cpu = dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                    seconds_per_step=round(sec, 3),
                    sample=f"the whole {args.workload} step (every sequence, every layer), "
-                          f"median of {args.oracle_reps} runs, NumPy {npver} fp64, BLAS 1 thread")
+                          f"median of {args.oracle_reps} runs, NumPy {np.__version__} fp64, "
+                          f"BLAS 1 thread")
 
     res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
@@ -270,7 +497,8 @@ def main():
                            step="append+attention per layer" if with_append else "attention"),
                us_per_call=per_call, step_bytes=step_bytes,
                frac_of_peak=round(value * 1e9 / PEAK_HBM, 4),
-               roofline=roofline, cpu_baseline=cpu, headline_uniform_8k=headline)
+               roofline=roofline, cpu_baseline=cpu, headline_uniform_8k=headline,
+               configs=configs)
     print(json.dumps(res), flush=True)
 
 
