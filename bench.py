@@ -284,7 +284,8 @@ def add_oracle(e, host):
 
 
 def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=50,
-                       graph=False, oracle_seqs=(0, 21, 42, 63), with_oracle=True):
+                       graph=False, oracle_seqs=(0, 21, 42, 63), with_oracle=True,
+                       fused=True):
     """The decode loop: 24 layers alternating ring-128 / paged full attention,
     batch 64, initial lengths 1024..32768, 50 steps each appending one token
     per sequence in every layer.  Timed as whole steps (all layers), eagerly
@@ -310,6 +311,11 @@ def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=
         # launches go to torch's current stream: the timed stream when eager,
         # the capture stream while a HIP graph is being recorded
         for m, o in zip(model, outs):
+            if fused:
+                sa.decode_attention_append(m.q, m.k_new, m.v_new, m.k_cache, m.v_cache,
+                                           m.block_table, lens, m.sinks, m.window, out=o,
+                                           workspace=ws, variant=variant)
+                continue
             sa.kv_append(m.k_new, m.v_new, m.k_cache, m.v_cache, m.block_table, lens, m.window)
             sa.decode_attention(m.q, m.k_cache, m.v_cache, m.block_table, lens, m.sinks,
                                 m.window, out=o, workspace=ws, variant=variant)
@@ -345,9 +351,10 @@ def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=
         cpu_step = oracle_seconds(hosts, 1) * B / len(oracle_seqs)
         note = (f"{len(oracle_seqs)} of {B} sequences, all {layers} layers, one step, scaled "
                 f"x{B / len(oracle_seqs):g}; NumPy fp64, 1 thread")
-    e = entry("decode_loop", f"step ({layers} layers: append + attention each)", us_step,
+    e = entry("decode_loop", f"step ({layers} layers: append + attention each, "
+              f"{'one launch' if fused else 'separate append launch'})", us_step,
               total / steps, cpu_step, note, steps=steps, layers=layers,
-              loop_ms=round(us_step * steps / 1e3, 3), hip_graph=graph)
+              loop_ms=round(us_step * steps / 1e3, 3), hip_graph=graph, fused_append=fused)
     del model, outs, ws
     torch.cuda.empty_cache()
     return e
@@ -366,6 +373,9 @@ def main():
     ap.add_argument("--oracle-reps", type=int, default=3)
     ap.add_argument("--configs", choices=("all", "none"), default="all",
                     help="also report every synthetic configuration (default: all)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with its own launch before each attention call instead of "
+                         "inside it")
     ap.add_argument("--graph", action="store_true",
                     help="replay the decode loop's step from a HIP graph")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -400,10 +410,22 @@ def main():
     splits = [sa.num_splits(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
                             variant=args.variant) for L in layers]
     with_append = args.workload == "batch64_ragged"
+    fused = with_append and not args.separate_append
 
     calls = []                               # (name, bytes, thunk) in step order
     for L, o, ws in zip(layers, outs, wss):
         lens = L.seq_lens.cpu().tolist()
+        if fused:
+            # the append happens inside the attention launch (rewriting the
+            # same slot with the same row on every repeat)
+            calls.append((f"append+attention(w={L.window})",
+                          attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim) +
+                          append_bytes(L.batch),
+                          lambda _=0, L=L, o=o, ws=ws: sa.decode_attention_append(
+                              L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                              L.seq_lens, L.sinks, L.window, out=o, workspace=ws,
+                              variant=args.variant, stream=stream)))
+            continue
         if with_append:
             calls.append((f"append(w={L.window})", append_bytes(L.batch),
                           lambda _=0, L=L: sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache,
@@ -438,13 +460,14 @@ def main():
         print(f"# {nm}: {us:.2f} us, {b / (us * 1e-6) / 1e9:.1f} GB/s", flush=True)
 
     # dominant kernel: the full-layer attention call
-    dom = 1 if with_append else 0
+    dom = 1 if with_append and not fused else 0
     dom_us = per_call[dom]["us_mean"]
     achieved = calls[dom][1] / (dom_us * 1e-6) / 1e9
     traffic = load_traffic() if args.workload == "batch64_ragged" and args.variant == 0 else None
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
                     frac=round(achieved * 1e9 / PEAK_HBM, 4), traffic=traffic,
-                    kernel=("decode_stream_kernel + combine_stream_kernel (one attention call)"
+                    kernel=("decode_stream_kernel + combine_stream_kernel (one attention call"
+                            + (", append inside)" if fused else ")")
                             if splits[0] > 1 and args.variant in (0, 4) else
                             "decode_mfma_kernel (+ combine_kernel when split)"),
                     algorithmic_bytes_per_launch=calls[dom][1], avg_launch_us=round(dom_us, 2))
@@ -470,7 +493,7 @@ def main():
             print(f"# {e['config']}: {e['us']} us, {e['gbps']} GB/s", flush=True)
         headline = configs[0]
         loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
-                                  with_oracle=oc)
+                                  with_oracle=oc, fused=not args.separate_append)
         configs.append(loop)
         print(f"# decode loop: {loop['us']} us per step, {loop['gbps']} GB/s", flush=True)
         if oc:                               # host timings after all GPU timings
@@ -494,7 +517,9 @@ def main():
                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
                config=dict(workload=args.workload, batch=64, q_heads=64, kv_heads=8, head_dim=64,
                            block_size=16, splits=splits, variant=args.variant,
-                           step="append+attention per layer" if with_append else "attention"),
+                           step=("append inside attention, one launch per layer" if fused
+                                 else "append + attention per layer" if with_append
+                                 else "attention")),
                us_per_call=per_call, step_bytes=step_bytes,
                frac_of_peak=round(value * 1e9 / PEAK_HBM, 4),
                roofline=roofline, cpu_baseline=cpu, headline_uniform_8k=headline,

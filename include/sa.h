@@ -153,6 +153,25 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
                         void* stream);
 
 /*
+ * The fused decode step (SimpleLLM README, optimisation table: one
+ * decode-attention kernel that also does the KV append): exactly
+ * sa_kv_append followed by sa_decode_attention with the same arguments, in
+ * one launch (plus the merge launch when the call is split).  The wavefront
+ * that attends the new token's slot stores k_new / v_new into the pools and
+ * takes the new token's K and V from k_new / v_new, so the pools after the
+ * call are bit-identical to those after sa_kv_append and the output is that
+ * of sa_decode_attention on them.  A new token whose slot is past the
+ * table's capacity is skipped, as by sa_kv_append.  Not available with
+ * SA_VARIANT_VALU.
+ */
+int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
+                               sa_bf16* k_cache, sa_bf16* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const float* sinks, int32_t window, sa_bf16* out,
+                               const sa_dims* dims, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Split-K partials only, for a caller that merges them itself (for example
  * across devices that each hold part of a context).  With S =
  * sa_decode_num_splits(dims, window), partition j of (b, h) covers attended

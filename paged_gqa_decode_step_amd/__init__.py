@@ -30,6 +30,7 @@ VARIANT_DEFAULT = 0
 VARIANT_MFMA_TWO_PASS = 1
 VARIANT_MFMA_FUSED = 2
 VARIANT_VALU = 3
+VARIANT_MFMA_BALANCED = 4
 
 
 class Dims(ctypes.Structure):
@@ -54,7 +55,8 @@ class SAError(RuntimeError):
 
 _lib = None
 EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
-           "sa_decode_attention", "sa_decode_partials", "sa_combine", "sa_status_string")
+           "sa_decode_attention", "sa_decode_attention_append", "sa_decode_partials",
+           "sa_combine", "sa_status_string")
 
 
 def load(path: Optional[str] = None):
@@ -77,6 +79,9 @@ def load(path: Optional[str] = None):
     lib.sa_decode_workspace_bytes.restype = sz
     lib.sa_decode_attention.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, dp, vp, sz, vp]
     lib.sa_decode_attention.restype = ctypes.c_int
+    lib.sa_decode_attention_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, dp, vp,
+                                               sz, vp]
+    lib.sa_decode_attention_append.restype = ctypes.c_int
     lib.sa_decode_partials.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, dp, vp]
     lib.sa_decode_partials.restype = ctypes.c_int
     lib.sa_combine.argtypes = [vp, vp, vp, i32, vp, dp, vp]
@@ -224,6 +229,39 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, sinks=None, win
                                     _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out),
                                     ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream))
     _raise(st, "sa_decode_attention")
+    return out
+
+
+def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                            sinks=None, window=0, out=None, workspace=None, num_splits=0,
+                            variant=VARIANT_DEFAULT, stream=None):
+    """The fused decode step: the KV append of k_new / v_new and the attention
+    over the updated cache, in one launch.  Returns ``out``."""
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    dev = q.device
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(k_new, "k_new", torch.bfloat16, 3, dev)
+    _check(v_new, "v_new", torch.bfloat16, 3, dev)
+    if tuple(k_new.shape) != (d.num_seqs, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != d.num_q_heads:
+            raise ValueError("sinks must have one entry per query head")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().sa_decode_attention_append(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d), _ptr(workspace),
+        ws_bytes, _stream(stream))
+    _raise(st, "sa_decode_attention_append")
     return out
 
 

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int h = g * a.G + c16;
     const bool head_ok = c16 < a.G;
 
-    int n = a.seq_lens[b];
+    const int L = a.seq_lens[b];
+    int n = L;
     if (a.window > 0) n = min(n, a.window);
     n = max(0, min(n, a.mbs << a.bs_log2));
     const int P = a.part_tokens;
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
 
     u32x4_t qop0, qop1;
     load_query(a, b, g, lane, qop0, qop1);
-    const Unit u = make_unit(a, b, g, lane);
+    const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n));
     State st;
     st.reset();
     attend<BSL>(u, t0, t1, qop0, qop1, st);

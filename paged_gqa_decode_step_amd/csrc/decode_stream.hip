@@ -110,7 +110,8 @@ void decode_stream_kernel(const DecodeArgs a) {
 
         u32x4_t qop0, qop1;
         load_query(a, b, g, lane, qop0, qop1);
-        const Unit u = make_unit(a, b, g, lane);
+        const int L = a.k_new ? __builtin_amdgcn_readfirstlane(a.seq_lens[b]) : 0;
+        const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n));
         State st;
         st.reset();
         attend<BSL>(u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1, st);

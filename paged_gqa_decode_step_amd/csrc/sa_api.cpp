@@ -229,18 +229,22 @@ size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window) {
     return workspace_layout(dims, window, p, choose_mode(dims, window, p)).total;
 }
 
-int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
-                        const int32_t* block_table, const int32_t* seq_lens,
-                        const float* sinks, int32_t window, sa_bf16* out,
-                        const sa_dims* dims, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Attention, and with k_new/v_new the KV append in the same launch.
+int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
+           const sa_bf16* k_cache, const sa_bf16* v_cache, const int32_t* block_table,
+           const int32_t* seq_lens, const float* sinks, int32_t window, sa_bf16* out,
+           const sa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
     int st = check_dims(dims, window);
     if (st != SA_OK) return st;
     if (dims->num_seqs == 0) return SA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return SA_ERR_INVALID_ARG;
     const bool valu = dims->variant == SA_VARIANT_VALU;
-    if (valu && dims->num_q_heads / dims->num_kv_heads > 8) return SA_ERR_UNSUPPORTED;
+    if (valu && (dims->num_q_heads / dims->num_kv_heads > 8 || k_new)) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
     const Mode mode = choose_mode(dims, window, p);
@@ -256,6 +260,12 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     a.seq_lens = seq_lens;
     a.sinks = sinks;
     a.out = out;
+    if (k_new) {
+        a.k_new = k_new;
+        a.v_new = v_new;
+        a.k_store = const_cast<uint16_t*>(k_cache);
+        a.v_store = const_cast<uint16_t*>(v_cache);
+    }
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     if (mode == Mode::kBalanced) {
@@ -288,6 +298,33 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
     c.Hq = a.Hq;
     c.num_splits = p.splits;
     return to_status(sa::launch_combine(c, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
+                        const int32_t* block_table, const int32_t* seq_lens,
+                        const float* sinks, int32_t window, sa_bf16* out,
+                        const sa_dims* dims, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    return decode(q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, sinks, window,
+                  out, dims, workspace, workspace_bytes, stream);
+}
+
+int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
+                               sa_bf16* k_cache, sa_bf16* v_cache,
+                               const int32_t* block_table, const int32_t* seq_lens,
+                               const float* sinks, int32_t window, sa_bf16* out,
+                               const sa_dims* dims, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    const int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!k_new || !v_new) return SA_ERR_INVALID_ARG;
+    return decode(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks, window, out,
+                  dims, workspace, workspace_bytes, stream);
 }
 
 int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,

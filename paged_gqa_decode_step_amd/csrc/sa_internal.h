@@ -35,6 +35,10 @@ struct DecodeArgs {
     const int32_t* block_table;
     const int32_t* seq_lens;
     const float* sinks;       // may be null
+    const uint16_t* k_new;    // non-null: append the new token in the same launch
+    const uint16_t* v_new;
+    uint16_t* k_store;        // the caches again, writable (with k_new)
+    uint16_t* v_store;
     uint16_t* out;            // kWriteOut, kFusedCombine
     float* part_o;            // kWritePartials, kFusedCombine
     float* part_lse;

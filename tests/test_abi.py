@@ -40,7 +40,7 @@ def good_dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
     assert set(names) == set(sa.EXPORTS)
@@ -76,6 +76,20 @@ def test_bad_dims_rejected_everywhere(lib, kw, status):
                                    ctypes.byref(d), FAKE, 1 << 30, None) == status
     assert lib.sa_decode_partials(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE,
                                   ctypes.byref(d), None) == status
+    assert lib.sa_decode_attention_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                          FAKE, ctypes.byref(d), FAKE, 1 << 30, None) == status
+
+
+def test_fused_append_needs_new_rows_and_an_mfma_variant(lib):
+    d = good_dims()
+    for i in (1, 2):                      # k_new, v_new
+        args = [FAKE] * 8
+        args[i] = None
+        assert lib.sa_decode_attention_append(*args, 0, FAKE, ctypes.byref(d), FAKE, 1 << 30,
+                                              None) == SA_ERR_INVALID_ARG
+    d = good_dims(variant=3)
+    assert lib.sa_decode_attention_append(*([FAKE] * 8), 0, FAKE, ctypes.byref(d), FAKE,
+                                          1 << 30, None) == SA_ERR_UNSUPPORTED
 
 
 def test_window_needs_room_in_the_table(lib):

@@ -21,7 +21,8 @@ def build_model(layers, B, seed, steps):
     return model, model[0].seq_lens.clone()
 
 
-def test_graph_replay_equals_eager(lib):
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_equals_eager(lib, fused):
     steps, layers, B = 4, 4, 8
     eager, lens_e = build_model(layers, B, 77, steps)
     graph_m, lens_g = build_model(layers, B, 77, steps)
@@ -32,6 +33,11 @@ def test_graph_replay_equals_eager(lib):
 
     def step(model, lens, outs, ws):
         for m, o in zip(model, outs):
+            if fused:
+                lib.decode_attention_append(m.q, m.k_new, m.v_new, m.k_cache, m.v_cache,
+                                            m.block_table, lens, m.sinks, m.window, out=o,
+                                            workspace=ws)
+                continue
             lib.kv_append(m.k_new, m.v_new, m.k_cache, m.v_cache, m.block_table, lens, m.window)
             lib.decode_attention(m.q, m.k_cache, m.v_cache, m.block_table, lens, m.sinks,
                                  m.window, out=o, workspace=ws)
