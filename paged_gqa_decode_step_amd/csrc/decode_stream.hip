@@ -49,7 +49,7 @@ __attribute__((amdgpu_waves_per_eu(SA_STREAM_OCC, SA_STREAM_OCC)))
 #endif
 void decode_stream_kernel(const DecodeArgs a) {
     extern __shared__ int s_mem[];
-    int* s_n = s_mem;              // attended slots of each sequence
+    int* s_len = s_mem;            // seq_lens (n and the appended token's slot follow)
     int* s_end = s_mem + a.B;      // inclusive prefix of Hkv * steps, in steps
     const int lane = threadIdx.x;
     const int i = blockIdx.x;
@@ -59,7 +59,8 @@ void decode_stream_kernel(const DecodeArgs a) {
     int carry = 0;
     for (int base = 0; base < a.B; base += 64) {
         const int b = base + lane;
-        const int n = b < a.B ? attended(a, a.seq_lens[b]) : 0;
+        const int L = b < a.B ? a.seq_lens[b] : 0;
+        const int n = attended(a, L);
         int v = ((n + kStepTokens - 1) / kStepTokens) * a.Hkv;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -68,7 +69,7 @@ void decode_stream_kernel(const DecodeArgs a) {
         }
         v += carry;
         if (b < a.B) {
-            s_n[b] = n;
+            s_len[b] = L;
             s_end[b] = v;
             if (i == 0) a.plan[b] = v;
         }
@@ -99,7 +100,8 @@ void decode_stream_kernel(const DecodeArgs a) {
     }
     int slot = 0;                 // 0: first unit of this wavefront, 1: last
     while (x < x1) {
-        const int n = __builtin_amdgcn_readfirstlane(s_n[b]);
+        const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
+        const int n = attended(a, L);
         const int steps = (n + kStepTokens - 1) / kStepTokens;
         const int end_b = __builtin_amdgcn_readfirstlane(s_end[b]);
         const int start_b = end_b - a.Hkv * steps;
@@ -110,7 +112,6 @@ void decode_stream_kernel(const DecodeArgs a) {
 
         u32x4_t qop0, qop1;
         load_query(a, b, g, lane, qop0, qop1);
-        const int L = a.k_new ? __builtin_amdgcn_readfirstlane(a.seq_lens[b]) : 0;
         const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n));
         State st;
         st.reset();
@@ -127,7 +128,7 @@ void decode_stream_kernel(const DecodeArgs a) {
         x = seg_end;
         if (x >= end_b) {         // next sequence that has any step
             ++b;
-            while (b < a.B && __builtin_amdgcn_readfirstlane(s_n[b]) == 0) ++b;
+            while (b < a.B && __builtin_amdgcn_readfirstlane(attended(a, s_len[b])) == 0) ++b;
         }
     }
 }

@@ -173,7 +173,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.v_lane = (unsigned)(u.c16 * bs) * 2;
     u.scale_log2 = a.scale_log2;
     u.new_slot = new_slot;
-    u.kn_row = a.k_new + ((size_t)b * a.Hkv + g) * kHeadDim;
+    u.kn_row = a.k_new + ((size_t)b * a.Hkv + g) * kHeadDim;   // read only with new_slot >= 0
     u.vn_row = a.v_new + ((size_t)b * a.Hkv + g) * kHeadDim;
     u.kstore = reinterpret_cast<char*>(a.k_store) + (size_t)g * bs * kHeadDim * 2;
     u.vstore = reinterpret_cast<char*>(a.v_store) + (size_t)g * bs * kHeadDim * 2;
@@ -213,30 +213,6 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
     const int nsteps = (t1 - t0 + kStepTokens - 1) / kStepTokens;
     const bool has_new = u.new_slot >= t0 && u.new_slot < t1;   // wave-uniform
 
-    // The append (the fused form of the KV append): the one run that holds
-    // the new token's slot stores its K row and V column into the pools.  No
-    // other wavefront of this launch reads that slot, and this one takes the
-    // new values from k_new / v_new (see compute_step), not from the pool.
-    if (has_new) {
-        const unsigned nblk_id =
-            (unsigned)__builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl);
-        const int noff = u.new_slot & (bs - 1);
-        if (c16 == 0) {
-            char* kp = u.kstore + (size_t)nblk_id * u.blk_stride + (unsigned)noff * kHeadDim * 2;
-            *reinterpret_cast<u32x4_t*>(kp + 16 * q4) =
-                *reinterpret_cast<const u32x4_t*>(u.kn_row + 8 * q4);
-            *reinterpret_cast<u32x4_t*>(kp + 64 + 16 * q4) =
-                *reinterpret_cast<const u32x4_t*>(u.kn_row + 32 + 8 * q4);
-        }
-        if (q4 == 0) {
-            char* vp = u.vstore + (size_t)nblk_id * u.blk_stride + (unsigned)noff * 2;
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *reinterpret_cast<uint16_t*>(vp + (size_t)(16 * j + c16) * bs * 2) =
-                    u.vn_row[16 * j + c16];
-        }
-    }
-
     // the 8 loads of step s (K: 2 M-tiles x 2 k-steps; V: 4 dim tiles)
     auto load_step = [&](int s, StepRegs& r) {
         const int base = t0 + (s << 5);
@@ -261,35 +237,6 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
     };
 
     auto compute_step = [&](int s, StepRegs& r) {
-        const int base = t0 + (s << 5);
-        if (has_new && u.new_slot >= base && u.new_slot < base + kStepTokens) {
-            // the step holding the new token: its K row and V elements come
-            // from k_new / v_new (the pool still held the old slot when loaded)
-            const int kslot = base + ((c16 >> 2) << 3) + (c16 & 3);   // M-tile 0 row
-            if (kslot == u.new_slot || kslot + 4 == u.new_slot) {
-                const u32x4_t kn0 = *reinterpret_cast<const u32x4_t*>(u.kn_row + 8 * q4);
-                const u32x4_t kn1 = *reinterpret_cast<const u32x4_t*>(u.kn_row + 32 + 8 * q4);
-                if (kslot == u.new_slot) {
-                    r.k[0] = kn0;
-                    r.k[1] = kn1;
-                } else {
-                    r.k[2] = kn0;
-                    r.k[3] = kn1;
-                }
-            }
-            const int e = u.new_slot - (base + (q4 << 3));            // element of this V^T run
-            if (e >= 0 && e < 8) {
-                const unsigned sh = (e & 1) * 16;
-                const unsigned keep = ~(0xFFFFu << sh);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const unsigned val = (unsigned)u.vn_row[16 * j + c16] << sh;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        if (w == (e >> 1)) r.v[j][w] = (r.v[j][w] & keep) | val;
-                }
-            }
-        }
         f32x4_t s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         s0 = mfma(r.k[0], qop0, s0);
         s0 = mfma(r.k[1], qop1, s0);
@@ -301,7 +248,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
             t[i] = s0[i] * u.scale_log2;
             t[4 + i] = s1[i] * u.scale_log2;
         }
-        const int tok = base + (q4 << 3);            // slot of t[0] on this lane
+        const int tok = t0 + (s << 5) + (q4 << 3);   // slot of t[0] on this lane
         if (tok + 8 > t1) {                           // only in a run's last step
             const int valid = max(0, min(8, t1 - tok));
 #pragma unroll
@@ -348,6 +295,27 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
     // ever reaches past the run and no load sits under a branch inside the
     // loop (a conditional load there would make the compiler wait for every
     // outstanding load at the join).
+    if (has_new) {
+        // The append (the fused form of the KV append): the one run that
+        // holds the new token's slot stores its K row and V column into the
+        // pools before it issues any load.  A wavefront's memory operations
+        // to one address complete in program order (and the compiler keeps
+        // the order: the pools are read and written through pointers that
+        // may alias), so this run's loads of that slot return the new row.
+        // No other wavefront of this launch reads the slot.
+        const int lane = c16 + 16 * q4;
+        const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
+        const uint16_t vval = u.vn_row[lane];
+        const unsigned nblk_id =
+            (unsigned)__builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl);
+        const unsigned noff = (unsigned)(u.new_slot & (bs - 1));
+        const size_t blk_off = (size_t)nblk_id * u.blk_stride;
+        // V column: lane = dim; K row: word `lane` of the 128-byte row
+        *reinterpret_cast<uint16_t*>(u.vstore + blk_off + ((unsigned)lane * bs + noff) * 2) = vval;
+        if (lane < 32)
+            *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * lane) = kword;
+    }
+
     StepRegs A, B;
     load_step(0, A);
     int s = 0;
