@@ -6,7 +6,9 @@
 // (b, g).  Laying the units out one after another gives T steps in all;
 // wavefront i of NW takes steps [i*T/NW, (i+1)*T/NW) and walks them unit by
 // unit.  A unit it covers whole gets its bf16 output (with the sink)
-// directly; a unit it covers in part leaves a partial (o, lse), which only
+// directly (a sequence with nothing to attend gets zeros from the wavefront
+// that finished the sequence before it, or from wavefront 0); a unit it
+// covers in part leaves a partial (o, lse), which only
 // its first and last unit can need, so each wavefront owns two partial slots.
 // combine_stream_kernel then merges, for each unit spread over wavefronts
 // i0..i1, the slots those wavefronts left (the log-sum-exp merge of the
@@ -14,9 +16,10 @@
 // names the online softmax it rests on).
 //
 // Every wavefront derives T and the unit layout itself from seq_lens (an
-// inclusive scan in LDS), so there is no planning launch; wavefront 0 also
-// stores the per-sequence step prefix for the combine kernel.  The per-step
-// MFMA machinery is mfma_attend.h.
+// inclusive scan in LDS), so there is no planning launch.  The wavefronts
+// holding a unit's first and last steps record, for the combine kernel, the
+// unit's first partial slot and its last wavefront.  The per-step MFMA
+// machinery is mfma_attend.h.
 #include "mfma_attend.h"
 
 namespace sa {
@@ -29,12 +32,21 @@ __device__ __forceinline__ int attended(const DecodeArgs& a, int L) {
     return max(0, min(n, a.mbs << a.bs_log2));
 }
 
-// first step of wavefront i, and the wavefront holding step x (T > 0)
+// first step of wavefront i (T > 0)
 __device__ __forceinline__ long long wave_start(long long i, long long T, long long NW) {
     return i * T / NW;
 }
-__device__ __forceinline__ long long wave_of(long long x, long long T, long long NW) {
-    return ((x + 1) * NW - 1) / T;
+
+// Sequence b has nothing to attend: zero outputs, and for each of its units a
+// record (first slot in wavefront i, last wavefront i) that the combine
+// kernel reads as "done".
+__device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, int lane) {
+    for (int g = 0; g < a.Hkv; ++g) write_zero(a, b, g, lane);
+    if (lane < a.Hkv) {
+        int* seg = a.unit_seg + 2 * (b * a.Hkv + lane);
+        seg[0] = 2 * i;
+        seg[1] = i;
+    }
 }
 
 // SA_STREAM_OCC > 0 asks the compiler for that many waves per SIMD.
@@ -71,7 +83,6 @@ void decode_stream_kernel(const DecodeArgs a) {
         if (b < a.B) {
             s_len[b] = L;
             s_end[b] = v;
-            if (i == 0) a.plan[b] = v;
         }
         carry = __shfl(v, 63);
     }
@@ -79,14 +90,21 @@ void decode_stream_kernel(const DecodeArgs a) {
     const long long T = carry;
     if (T == 0) {
         // nothing attended anywhere: every output is 0
-        for (int u = i; u < a.B * a.Hkv; u += NW) write_zero(a, u / a.Hkv, u % a.Hkv, lane);
+        for (int bz = i; bz < a.B; bz += NW) finish_empty(a, bz, i, lane);
         return;
     }
     // step counts stay below 2^31 (sequences x KV heads x 2^26 slots / 32),
     // so the walk runs on 32-bit wave-uniform values
-    int x = (int)wave_start(i, T, NW);
-    const int x1 = (int)wave_start(i + 1, T, NW);
-    if (x >= x1) return;
+    if (i == 0)                   // sequences before the first with a step
+        for (int bz = 0; bz < a.B && s_end[bz] == 0; ++bz) finish_empty(a, bz, 0, lane);
+    // The launch sizes NW from the table's capacity; with fewer steps than
+    // that, only the first T wavefronts take part, so that every wavefront
+    // in use holds at least one step and the wavefronts a unit spans are
+    // consecutive ones that each left it a segment.
+    const long long NWe = T < NW ? T : (long long)NW;
+    if (i >= NWe) return;
+    int x = (int)wave_start(i, T, NWe);
+    const int x1 = (int)wave_start(i + 1, T, NWe);
 
     // sequence holding step x: the first b with s_end[b] > x
     int b;
@@ -117,6 +135,11 @@ void decode_stream_kernel(const DecodeArgs a) {
         st.reset();
         attend<BSL>(u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1, st);
         const float l_tot = st.total();
+        if (lane == 0) {
+            int* seg = a.unit_seg + 2 * (b * a.Hkv + g);
+            if (s0 == 0) seg[0] = 2 * i + slot;    // this wavefront's slot for the unit
+            if (s1 == steps) seg[1] = i;
+        }
         if (s0 == 0 && s1 == steps) {
             write_out(a, b, g, lane, st, l_tot);
         } else {
@@ -128,17 +151,23 @@ void decode_stream_kernel(const DecodeArgs a) {
         x = seg_end;
         if (x >= end_b) {         // next sequence that has any step
             ++b;
-            while (b < a.B && __builtin_amdgcn_readfirstlane(attended(a, s_len[b])) == 0) ++b;
+            while (b < a.B && __builtin_amdgcn_readfirstlane(attended(a, s_len[b])) == 0) {
+                finish_empty(a, b, i, lane);
+                ++b;
+            }
         }
     }
 }
 
 // One workgroup per (b, h) of a unit spread over wavefronts i0 < i1: merge
 // the partial slots those wavefronts left, with the sink.  Units done whole
-// by one wavefront were written by the partition kernel; units with no step
-// get 0 here.  Each wavefront merges its share of the segments with a
-// running maximum, so all of a segment's loads (lse and o row) can be in
-// flight at once: two memory round trips in all (plan, then partials).
+// by one wavefront, and units with no step, were written by the partition
+// kernel.  Two memory round trips: the unit's segment record, then its
+// partials, kCombineChunk segments per wavefront at a time with
+// every load issued before any is used (indices past the last segment are
+// clamped to it and weighted 0, so no load sits under a branch).
+constexpr int kCombineChunk = 16;
+
 template <int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const DecodeArgs a) {
     __shared__ float s_num[WAVES][64];
@@ -151,34 +180,38 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     const int h = bh - b * a.Hq;
     const int g = h / a.G;
     const int hl = h - g * a.G;
-    const long long T = a.plan[a.B - 1];
-    const long long end_b = a.plan[b];
-    const long long prev = b > 0 ? a.plan[b - 1] : 0;
-    const int steps = (int)((end_b - prev) / a.Hkv);
-    uint16_t* op = a.out + (size_t)bh * kHeadDim + lane;
-    if (steps == 0) {
-        if (w == 0) *op = 0;
-        return;
-    }
-    const long long NW = a.num_waves;
-    const long long us = prev + (long long)g * steps;
-    const long long i0 = wave_of(us, T, NW);
-    const long long i1 = wave_of(us + steps - 1, T, NW);
-    if (i0 == i1) return;                         // written whole by one wavefront
-    const int first_slot = wave_start(i0, T, NW) == us ? 0 : 1;
-    const int nseg = (int)(i1 - i0 + 1);
-    // segment k is wavefront i0 + k; its slot is 2*(i0+k) + (k == 0 ? first_slot : 0)
+    const int2 rec = *reinterpret_cast<const int2*>(a.unit_seg + 2 * (b * a.Hkv + g));
+    // every unit's record is written by this call; the clamps only keep a
+    // damaged one from reading past the partial slots
+    const int first = min(max(rec.x, 0), 2 * a.num_waves - 1);
+    const int i0 = first >> 1;
+    const int i1 = min(max(rec.y, i0), a.num_waves - 1);
+    if (i0 == i1) return;                         // written whole (or zero) by one wavefront
+    const int nseg = i1 - i0 + 1;
+    // segment k is wavefront i0 + k; its slot is `first` for k = 0, else 2*(i0+k)
     float M = -INFINITY, num = 0.f, den = 0.f;
-#pragma unroll 8
-    for (int k = w; k < nseg; k += WAVES) {
-        const size_t sl = (size_t)(2 * (i0 + k) + (k == 0 ? first_slot : 0)) * a.G + hl;
-        const float l = a.part_lse[sl];
-        const float o = a.part_o[sl * kHeadDim + lane];
-        const float M2 = fmaxf(M, l);
+    for (int k0 = w * kCombineChunk; k0 < nseg; k0 += WAVES * kCombineChunk) {
+        float l[kCombineChunk], o[kCombineChunk];
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) {
+            const int k = min(k0 + j, nseg - 1);
+            const size_t sl = (size_t)(k == 0 ? first : 2 * (i0 + k)) * a.G + hl;
+            l[j] = a.part_lse[sl];
+            o[j] = a.part_o[sl * kHeadDim + lane];
+        }
+        float M2 = M;
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) M2 = fmaxf(M2, k0 + j < nseg ? l[j] : -INFINITY);
         const float r = __builtin_amdgcn_exp2f((M - M2) * kLog2e);   // 0 while M = -inf
-        const float wt = __builtin_amdgcn_exp2f((l - M2) * kLog2e);
-        num = num * r + wt * o;
-        den = den * r + wt;
+        float cn = 0.f, cd = 0.f;
+#pragma unroll
+        for (int j = 0; j < kCombineChunk; ++j) {
+            const float wt = k0 + j < nseg ? __builtin_amdgcn_exp2f((l[j] - M2) * kLog2e) : 0.f;
+            cn += wt * o[j];
+            cd += wt;
+        }
+        num = num * r + cn;
+        den = den * r + cd;
         M = M2;
     }
     if (WAVES > 1) {
@@ -208,7 +241,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     const float r = __builtin_amdgcn_exp2f((M - M2) * kLog2e);
     den = den * r + __builtin_amdgcn_exp2f((sig - M2) * kLog2e);
     const __bf16 o = (__bf16)(num * r / den);
-    *op = __builtin_bit_cast(uint16_t, o);
+    a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, o);
 }
 
 }  // namespace
@@ -229,7 +262,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
     const long long units = (long long)a.B * a.Hkv;
     const long long per_unit = (a.num_waves + units - 1) / units + 1;
     const dim3 cgrid((unsigned)a.B * a.Hq);
-    if (per_unit <= 8)
+    if (per_unit <= kCombineChunk * 3 / 4)
         hipLaunchKernelGGL(combine_stream_kernel<1>, cgrid, dim3(64), 0, stream, a);
     else if (per_unit <= 64)
         hipLaunchKernelGGL(combine_stream_kernel<4>, cgrid, dim3(256), 0, stream, a);

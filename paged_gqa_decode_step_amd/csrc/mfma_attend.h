@@ -132,7 +132,8 @@ struct Unit {
     const char* kbase;       // K pool + g * (bs*D*2)
     const char* vbase;       // V pool + g * (bs*D*2)
     // the token appended by this launch: its slot (-1: none), its K and V rows
-    // (k_new / v_new of this unit) and where the pools are written
+    // (k_new / v_new of this unit; q when nothing is appended, so that the
+    // rows can be read unconditionally) and where the pools are written
     int new_slot;
     const uint16_t* kn_row;
     const uint16_t* vn_row;
@@ -144,6 +145,7 @@ struct Unit {
     unsigned v_lane;         // c16 dim rows, bytes
     int bs_log2;
     int num_blocks;
+    int mbs;                 // entries in a block-table row
     int c16, q4;
     float scale_log2;
 };
@@ -165,6 +167,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.q4 = lane >> 4;
     u.bs_log2 = a.bs_log2;    // == BSL of the kernel instantiation
     u.num_blocks = a.num_blocks;
+    u.mbs = a.mbs;
     u.blk_stride = (unsigned)(a.Hkv * bs * kHeadDim * 2);
     u.kbase = reinterpret_cast<const char*>(a.k_cache) + (size_t)g * bs * kHeadDim * 2;
     u.vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * bs * kHeadDim * 2;
@@ -173,8 +176,9 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.v_lane = (unsigned)(u.c16 * bs) * 2;
     u.scale_log2 = a.scale_log2;
     u.new_slot = new_slot;
-    u.kn_row = a.k_new + ((size_t)b * a.Hkv + g) * kHeadDim;   // read only with new_slot >= 0
-    u.vn_row = a.v_new + ((size_t)b * a.Hkv + g) * kHeadDim;
+    const size_t row = ((size_t)b * a.Hkv + g) * kHeadDim;
+    u.kn_row = a.k_new ? a.k_new + row : a.q;
+    u.vn_row = a.k_new ? a.v_new + row : a.q;
     u.kstore = reinterpret_cast<char*>(a.k_store) + (size_t)g * bs * kHeadDim * 2;
     u.vstore = reinterpret_cast<char*>(a.v_store) + (size_t)g * bs * kHeadDim * 2;
     return u;
@@ -194,24 +198,32 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, in
     }
 }
 
+// Block-table entries blk0 + lane of a unit, one per lane, clamped into the
+// pool (lanes past the row's end repeat its last entry; they are never used).
+// No branch around the load, so it is in flight with whatever precedes it.
+__device__ __forceinline__ int table_slice(const Unit& u, int blk0, int lane) {
+    const int e = u.bt_row[min(blk0 + lane, u.mbs - 1)];
+    return min(max(e, 0), u.num_blocks - 1);
+}
+
 // Attend over slots [t0, t1) of one unit (t0 a multiple of 32, t1 > t0, and
-// the run spanning at most kMaxTableSlice blocks), folding into st.
+// the run spanning at most kMaxTableSlice blocks, whose table entries tbl
+// holds), folding into st.  kword / vval: this lane's word (lane & 31) of the
+// new token's K row and its element `lane` of the V row.
 template <int BSL>
-__device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_t qop0,
+__device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl,
+                                           unsigned kword, uint16_t vval, u32x4_t qop0,
                                            u32x4_t qop1, State& st) {
     const int c16 = u.c16, q4 = u.q4;
     constexpr int bs = 1 << BSL;
-    // block-table slice of this run, one entry per lane
     const int blk0 = t0 >> BSL;
-    const int nblk = ((t1 - 1) >> BSL) - blk0 + 1;
-    int tbl = 0;
-    if (c16 + 16 * q4 < nblk) {
-        tbl = u.bt_row[blk0 + c16 + 16 * q4];
-        tbl = min(max(tbl, 0), u.num_blocks - 1);
-    }
     const int last_chunk = (t1 - 1) & ~7;
     const int nsteps = (t1 - t0 + kStepTokens - 1) / kStepTokens;
     const bool has_new = u.new_slot >= t0 && u.new_slot < t1;   // wave-uniform
+    // block of the new slot (any lane when there is none: bpermute wraps),
+    // outside the branch so the table wait is not merged into the join below
+    const unsigned nblk_id =
+        (unsigned)__builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl);
 
     // the 8 loads of step s (K: 2 M-tiles x 2 k-steps; V: 4 dim tiles)
     auto load_step = [&](int s, StepRegs& r) {
@@ -289,35 +301,40 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
         st.m = m_new;
     };
 
+    // The append (the fused form of the KV append): the one run that holds
+    // the new token's slot stores its K row and V column into the pools
+    // before it issues the loads of the step holding that slot.  A
+    // wavefront's memory operations to one address complete in program order
+    // (and the compiler keeps the order: the pools are read and written
+    // through pointers that may alias), so this run's loads of the slot
+    // return the new row.  No other wavefront of this launch reads the slot.
+    // When the slot is past the first step, the store goes after the first
+    // step's loads (step 1 onwards is loaded later), so any wait on the store
+    // overlaps with those loads.  (The V column is one 2-byte element in each
+    // of 64 dim rows; rewriting the block's whole [D][bs] segment instead, to
+    // write whole cache lines, measured slower.)
+    auto store_new = [&]() {
+        const int lane = c16 + 16 * q4;
+        const unsigned noff = (unsigned)(u.new_slot & (bs - 1));
+        const size_t blk_off = (size_t)nblk_id * u.blk_stride;
+        // V column: lane = dim.  K row: word (lane & 31) of the 128-byte row
+        // (the upper half-wave stores the same words again).
+        *reinterpret_cast<uint16_t*>(u.vstore + blk_off + ((unsigned)lane * bs + noff) * 2) = vval;
+        *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
+            kword;
+    };
+    const bool new_first = has_new && u.new_slot < t0 + kStepTokens;
+    if (new_first) store_new();
+
     // Two register sets in ping-pong: the loads of step s+1 are in flight
     // while step s computes.  The loop covers whole pairs that still have a
     // next step to prefetch; the last one or two steps are peeled, so no load
     // ever reaches past the run and no load sits under a branch inside the
     // loop (a conditional load there would make the compiler wait for every
     // outstanding load at the join).
-    if (has_new) {
-        // The append (the fused form of the KV append): the one run that
-        // holds the new token's slot stores its K row and V column into the
-        // pools before it issues any load.  A wavefront's memory operations
-        // to one address complete in program order (and the compiler keeps
-        // the order: the pools are read and written through pointers that
-        // may alias), so this run's loads of that slot return the new row.
-        // No other wavefront of this launch reads the slot.
-        const int lane = c16 + 16 * q4;
-        const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
-        const uint16_t vval = u.vn_row[lane];
-        const unsigned nblk_id =
-            (unsigned)__builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl);
-        const unsigned noff = (unsigned)(u.new_slot & (bs - 1));
-        const size_t blk_off = (size_t)nblk_id * u.blk_stride;
-        // V column: lane = dim; K row: word `lane` of the 128-byte row
-        *reinterpret_cast<uint16_t*>(u.vstore + blk_off + ((unsigned)lane * bs + noff) * 2) = vval;
-        if (lane < 32)
-            *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * lane) = kword;
-    }
-
     StepRegs A, B;
     load_step(0, A);
+    if (has_new && !new_first) store_new();
     int s = 0;
     for (; s + 2 < nsteps; s += 2) {
         load_step(s + 1, B);
@@ -338,13 +355,24 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, u32x4_
 }
 
 // Attend over slots [t0, t1) of one unit in runs of at most kMaxTableSlice
-// blocks (t0 a multiple of 32).
+// blocks (t0 a multiple of 32).  The first run's table slice and the new
+// token's words are read here, with no branch, so they travel with the
+// caller's query loads.
 template <int BSL>
 __device__ __forceinline__ void attend(const Unit& u, int t0, int t1, u32x4_t qop0,
                                        u32x4_t qop1, State& st) {
     constexpr int run = kMaxTableSlice << BSL;
-    for (int r0 = t0; r0 < t1; r0 += run)
-        attend_run<BSL>(u, r0, min(t1, r0 + run), qop0, qop1, st);
+    const int lane = u.c16 + 16 * u.q4;
+    int tbl = table_slice(u, t0 >> BSL, lane);
+    const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
+    const uint16_t vval = u.vn_row[lane];
+    for (int r0 = t0;;) {
+        const int r1 = min(t1, r0 + run);
+        attend_run<BSL>(u, r0, r1, tbl, kword, vval, qop0, qop1, st);
+        if (r1 >= t1) break;
+        r0 = r1;
+        tbl = table_slice(u, r0 >> BSL, lane);
+    }
 }
 
 // bf16 output of the unit's heads with the sink in the denominator:

@@ -107,7 +107,7 @@ constexpr int kCounterSlots = 1 << 16;   // (sequence, KV head) pairs a fused ca
 constexpr size_t kCounterBytes = (size_t)kCounterSlots * sizeof(int32_t);
 
 struct WorkspaceLayout {
-    size_t part_o, part_lse, counters, plan, total;
+    size_t part_o, part_lse, counters, unit_seg, total;
 };
 
 enum class Mode { kStatic, kFused, kBalanced };
@@ -161,8 +161,8 @@ WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p
     w.counters = 0;
     w.part_o = kCounterBytes;
     w.part_lse = w.part_o + align256(rows * kHeadDim * sizeof(float));
-    w.plan = w.part_lse + align256(lse * sizeof(float));
-    w.total = w.plan + align256((size_t)d->num_seqs * sizeof(int32_t));
+    w.unit_seg = w.part_lse + align256(lse * sizeof(float));
+    w.total = w.unit_seg + align256((size_t)d->num_seqs * d->num_kv_heads * 2 * sizeof(int32_t));
     return w;
 }
 
@@ -271,7 +271,7 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     if (mode == Mode::kBalanced) {
         a.part_o = (float*)(ws + wl.part_o);
         a.part_lse = (float*)(ws + wl.part_lse);
-        a.plan = (int32_t*)(ws + wl.plan);
+        a.unit_seg = (int32_t*)(ws + wl.unit_seg);
         a.num_waves = (int32_t)stream_waves(dims, window);
         return to_status(sa::launch_decode_stream(a, s));
     }

@@ -43,7 +43,8 @@ struct DecodeArgs {
     float* part_o;            // kWritePartials, kFusedCombine
     float* part_lse;
     int32_t* counters;        // kFusedCombine: [B*Hkv], zero between calls
-    int32_t* plan;            // balanced kernel: [B] step prefix, for its combine
+    int32_t* unit_seg;        // balanced kernel: [B*Hkv][2] = (first partial slot, last
+                              // wavefront) of each unit with a step, for its combine
     int32_t num_waves;        // balanced kernel: wavefronts in the grid
     int32_t B, Hq, Hkv, G;
     int32_t bs_log2, mbs, num_blocks, window;

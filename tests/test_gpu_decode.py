@@ -265,3 +265,53 @@ def test_balanced_kernel_edge_cases(lib, W, B, lo, hi):
         a = attend(lib, layer, variant=v)
         assert_parity(out_f64(a), ref, f"balanced B={B} W={W} v={v}")
         assert torch.equal(a, attend(lib, layer, variant=v)), "not deterministic"
+
+
+@pytest.mark.parametrize("lens", [[0, 0, 700, 0, 33, 0], [0, 0, 0], [900, 0, 0], [0, 5000],
+                                  [0] * 70 + [129]])
+def test_empty_sequences_zeroed_over_stale_state(lib, lens):
+    """Empty sequences before the first one with a step, between two, after
+    the last, and a batch with nothing at all: zeros land over an output
+    prefilled with NaN, with a workspace that a call on other lengths has
+    left dirty (the merge must read only what this call recorded)."""
+    B = len(lens)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    cap = [max(3000, L) for L in lens]
+    dirty = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=[3000] * B, capacity=cap, seed=1300 + B, device="cuda")
+    layer = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=lens, capacity=cap, seed=1400 + B, device="cuda")
+    ref = oracle_attention(layer)
+    for v in (0, 4):
+        lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
+                             dirty.seq_lens, dirty.sinks, 0, workspace=ws, variant=v)
+        out = torch.full_like(layer.q, float("nan"))
+        lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                             layer.seq_lens, layer.sinks, 0, out=out, workspace=ws, variant=v)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, f"lens={lens} v={v}")
+
+
+@pytest.mark.parametrize("W", [0, 128])
+def test_short_sequences_under_a_large_capacity(lib, W):
+    """Tables sized for long contexts (8192 slots) holding short ones: the
+    launch plans for far more steps than there are, so most wavefronts have
+    nothing to do and a unit's steps must still be merged from exactly the
+    wavefronts that hold them (also after a call that dirtied the workspace)."""
+    B = 64
+    lens = synth.ragged_lengths(1500 + W, B, 1, 300)
+    cap = [8192] * B
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    dirty = synth.make_layer(batch=B, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[8192] * B, capacity=cap, window=W, seed=1600 + W,
+                             device="cuda")
+    layer = synth.make_layer(batch=B, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=lens, capacity=cap, window=W, seed=1700 + W, device="cuda")
+    ref = oracle_attention(layer)
+    for v in (0, 4):
+        lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
+                             dirty.seq_lens, dirty.sinks, W, workspace=ws, variant=v)
+        out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                                   layer.seq_lens, layer.sinks, W, workspace=ws, variant=v)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, f"short under capacity W={W} v={v}")
