@@ -273,6 +273,22 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
     return e, host
 
 
+def read_ceiling(sa, torch, timer, dev, nbytes=4 << 30):
+    """The practical HBM read ceiling: the library's plain streaming-read probe
+    over a 4 GiB buffer (far past the Infinity Cache)."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    f = lambda _=0: sa.read_bandwidth_probe(x, sink)                      # noqa: E731
+    timer.settle(f, 5)
+    us = timer.mean_us(f, 20)
+    del x
+    torch.cuda.empty_cache()
+    return dict(kernel="sa_read_bandwidth_probe (16-byte non-temporal streaming read)",
+                bytes=nbytes, us=round(us, 1), gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4))
+
+
 def add_oracle(e, host):
     """Time the oracle on the saved host inputs and add it to the entry."""
     h, scale, reps = host
@@ -488,6 +504,11 @@ def main():
                             "decode_mfma_kernel (+ combine_kernel when split)"),
                     algorithmic_bytes_per_launch=calls[dom][1], avg_launch_us=round(dom_us, 2))
 
+    ceiling = read_ceiling(sa, torch, timer, dev)
+    roofline["frac_of_read_ceiling"] = round(achieved * 1e9 / (ceiling["gbps"] * 1e9), 4)
+    print(f"# read ceiling: {ceiling['gbps']} GB/s ({ceiling['frac_of_peak']:.1%} of peak)",
+          flush=True)
+
     main_hosts = None if args.no_cpu_baseline else [host_inputs(L) for L in layers]
     del calls, layers, outs, wss
     torch.cuda.empty_cache()
@@ -511,11 +532,21 @@ def main():
         loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
                                   with_oracle=oc, fused=not args.separate_append)
         configs.append(loop)
+        hosts.append(None)                   # (its oracle is timed inside decode_loop_config)
         print(f"# decode loop: {loop['us']} us per step, {loop['gbps']} GB/s", flush=True)
+        if not args.graph:                   # the same loop replayed from a HIP graph per step
+            gl = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=True,
+                                    with_oracle=False, fused=not args.separate_append)
+            gl["config"] = "decode_loop (HIP graph)"
+            configs.append(gl)
+            hosts.append(None)
+            print(f"# decode loop, HIP graph: {gl['us']} us per step, {gl['gbps']} GB/s",
+                  flush=True)
         if oc:                               # host timings after all GPU timings
             print("# timing the oracle on the configurations...", flush=True)
             for e, h in zip(configs, hosts):
-                add_oracle(e, h)
+                if h is not None:
+                    add_oracle(e, h)
 
     cpu = None
     if main_hosts is not None:
@@ -538,7 +569,8 @@ def main():
                                  else "attention")),
                us_per_call=per_call, step_bytes=step_bytes,
                frac_of_peak=round(value * 1e9 / PEAK_HBM, 4),
-               roofline=roofline, cpu_baseline=cpu, headline_uniform_8k=headline,
+               roofline=roofline, cpu_baseline=cpu, read_ceiling=ceiling,
+               headline_uniform_8k=headline,
                configs=configs)
     print(json.dumps(res), flush=True)
 

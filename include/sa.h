@@ -196,6 +196,17 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
                int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream);
 
+/*
+ * Measurement helper, not a step of the decode path: reads `bytes` of device
+ * memory at `data` once, as a plain streaming read (16-byte non-temporal
+ * loads, the hint the decode kernels' K/V loads carry), and XORs every 32-bit
+ * word of it into *sink (device memory; the caller sets its start value,
+ * normally 0).  Its bandwidth is the practical HBM read ceiling the decode
+ * kernels are compared against.  bytes must be a multiple of 16 (0 launches
+ * nothing); data 16-byte aligned.
+ */
+int sa_read_bandwidth_probe(const void* data, size_t bytes, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* sa_status_string(int status);
 

@@ -56,7 +56,7 @@ class SAError(RuntimeError):
 _lib = None
 EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
            "sa_decode_attention", "sa_decode_attention_append", "sa_decode_partials",
-           "sa_combine", "sa_status_string")
+           "sa_combine", "sa_read_bandwidth_probe", "sa_status_string")
 
 
 def load(path: Optional[str] = None):
@@ -86,6 +86,8 @@ def load(path: Optional[str] = None):
     lib.sa_decode_partials.restype = ctypes.c_int
     lib.sa_combine.argtypes = [vp, vp, vp, i32, vp, dp, vp]
     lib.sa_combine.restype = ctypes.c_int
+    lib.sa_read_bandwidth_probe.argtypes = [vp, sz, vp, vp]
+    lib.sa_read_bandwidth_probe.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -309,3 +311,15 @@ def combine(part_o, part_lse, sinks=None, out=None, stream=None):
                            ctypes.byref(d), _stream(stream))
     _raise(st, "sa_combine")
     return out
+
+
+def read_bandwidth_probe(data, sink, stream=None):
+    """Stream-read every byte of ``data`` once (the HBM read ceiling probe),
+    XOR-folding its 32-bit words into ``sink`` (int32 device tensor, one
+    element, start value set by the caller)."""
+    if not isinstance(data, torch.Tensor) or not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous GPU tensor")
+    _check(sink, "sink", torch.int32, 1, data.device)
+    nbytes = data.numel() * data.element_size()
+    st = load().sa_read_bandwidth_probe(_ptr(data), nbytes, _ptr(sink), _stream(stream))
+    _raise(st, "sa_read_bandwidth_probe")

@@ -67,5 +67,6 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_read_probe(const void* data, size_t bytes, unsigned* sink, hipStream_t stream);
 
 }  // namespace sa

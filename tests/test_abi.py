@@ -40,7 +40,7 @@ def good_dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
     assert set(names) == set(sa.EXPORTS)
@@ -153,3 +153,11 @@ def test_split_table_is_fixed_and_bounded(lib):
         assert 1 <= s <= max(want, 8192 // 1024) and s <= 8192 // 32
     d.num_splits = 1
     assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == 8   # partitions are at most 1024 slots
+
+
+def test_read_probe_validates(lib):
+    sink = ctypes.c_void_p(0x20000)
+    assert lib.sa_read_bandwidth_probe(FAKE, 16, None, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_bandwidth_probe(None, 16, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_bandwidth_probe(FAKE, 20, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_bandwidth_probe(FAKE, 0, sink, None) == 0     # nothing launched
