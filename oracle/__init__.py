@@ -14,6 +14,9 @@ computes. It exists to check the HIP library, never to stand in for it:
   print no formula, so each definition below is the plain textbook reading
   of the named concept; every such reading is listed in the design doc.
 
+``oracle.rope`` adds the decode step with the rotary position embedding of
+the new token's query and key (page 1 lists RoPE as one fused kernel).
+
 Pins (tests/test_oracle_*.py, ``-m "not gpu"``): a pure-Python brute force
 over a layout-free history, torch's fp64 ``scaled_dot_product_attention``
 with the sink as an extra key, closed forms, invariants, a hand-derived
@@ -32,3 +35,4 @@ from .decode_step import (  # noqa: F401
     combine,
     kv_append,
 )
+from . import rope  # noqa: F401,E402
