@@ -289,6 +289,61 @@ def read_ceiling(sa, torch, timer, dev, nbytes=4 << 30):
                 frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4))
 
 
+def rope_step_config(sa, torch, timer, dev, steps, warmup, variant, with_oracle=True):
+    """The batch-64 ragged step (paged full layer + ring-128 layer, append
+    inside) with the rotary embedding of q and k_new fused in, beside the same
+    step without it on the same inputs."""
+    import numpy as np
+    layers = make_workload("batch64_ragged", dev)
+    P = max(int(L.seq_lens.max()) for L in layers) + 1
+    inv = 10000.0 ** (-np.arange(32, dtype=np.float64) * 2.0 / 64)
+    ang = np.arange(P, dtype=np.float64)[:, None] * inv[None, :]
+    cos_t = torch.from_numpy(np.cos(ang).astype(np.float32)).to(dev)
+    sin_t = torch.from_numpy(np.sin(ang).astype(np.float32)).to(dev)
+    outs = [torch.empty_like(L.q) for L in layers]
+    wss = [sa.new_workspace(L.q, L.k_cache, L.v_cache, L.block_table, L.window, variant=variant)
+           for L in layers]
+
+    def step_rope(_=0):
+        for L, o, ws in zip(layers, outs, wss):
+            sa.decode_attention_append_rope(L.q, L.k_new, L.v_new, L.k_cache, L.v_cache,
+                                            L.block_table, L.seq_lens, cos_t, sin_t,
+                                            style=sa.ROPE_HALF, sinks=L.sinks, window=L.window,
+                                            out=o, workspace=ws, variant=variant)
+
+    def step_plain(_=0):
+        for L, o, ws in zip(layers, outs, wss):
+            sa.decode_attention_append(L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                                       L.seq_lens, L.sinks, L.window, out=o, workspace=ws,
+                                       variant=variant)
+    nbytes = sum(attn_bytes(L.seq_lens.cpu().tolist(), L.window) + append_bytes(L.batch)
+                 for L in layers)
+    timer.settle(step_plain, warmup)
+    us_plain = timer.mean_us(step_plain, steps)
+    timer.settle(step_rope, warmup)
+    us_rope = timer.mean_us(step_rope, steps)
+    e = entry("batch64_ragged + RoPE", "step (both layers: RoPE, append and attention in one "
+              "launch each, half-split pairing)", us_rope, nbytes,
+              us_without_rope=round(us_plain, 2),
+              rope_overhead=round(us_rope / us_plain - 1.0, 4))
+    if with_oracle:
+        import oracle
+        hs = [host_inputs(L) for L in layers]
+        c_np, s_np = cos_t.cpu().numpy(), sin_t.cpu().numpy()
+        with one_blas_thread():
+            t0 = time.perf_counter()
+            for L, h in zip(layers, hs):
+                oracle.rope.decode_step_rope(h["q"], h["k"], h["v"], h["kn"], h["vn"], h["bt"],
+                                             h["lens"], h["sinks"], h["w"], c_np, s_np, "half")
+            cpu_s = time.perf_counter() - t0
+        e.update(oracle_s=round(cpu_s, 4), oracle_gbps=round(nbytes / cpu_s / 1e9, 4),
+                 oracle_sample="the whole step, once; NumPy fp64 (rotation in float32), 1 thread",
+                 gpu_speedup_vs_oracle=round(cpu_s / (us_rope * 1e-6), 1))
+    del layers, outs, wss
+    torch.cuda.empty_cache()
+    return e
+
+
 def add_oracle(e, host):
     """Time the oracle on the saved host inputs and add it to the entry."""
     h, scale, reps = host
@@ -529,6 +584,12 @@ def main():
             hosts.append(h)
             print(f"# {e['config']}: {e['us']} us, {e['gbps']} GB/s", flush=True)
         headline = configs[0]
+        rs = rope_step_config(sa, torch, timer, dev, args.steps, args.warmup, args.variant,
+                              with_oracle=oc)
+        configs.append(rs)
+        hosts.append(None)
+        print(f"# RoPE step: {rs['us']} us ({rs['us_without_rope']} without), {rs['gbps']} GB/s",
+              flush=True)
         loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
                                   with_oracle=oc, fused=not args.separate_append)
         configs.append(loop)

@@ -172,6 +172,43 @@ int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_
                                void* stream);
 
 /*
+ * Rotary position embedding of the new token (SimpleLLM README, optimisation
+ * table: RoPE as one fused kernel).  Pair i of a head vector's D dims is
+ * turned by the angle whose cosine and sine are cos_table[p][i] and
+ * sin_table[p][i] at the token's position p = L-1 (rows past the tables' end
+ * use the last row):  (x1, x2) -> (x1 cos - x2 sin, x2 cos + x1 sin), each
+ * product and sum rounded to float32 on its own, the result rounded to bf16
+ * (nearest, ties to even).  Pairing: SA_ROPE_HALF pairs dim i with dim
+ * i + D/2; SA_ROPE_INTERLEAVED pairs dims 2i and 2i+1.  The tables are
+ * device fp32 [max_positions][head_dim/2], 16-byte aligned, owned by the
+ * caller.
+ */
+#define SA_ROPE_HALF 0
+#define SA_ROPE_INTERLEAVED 1
+
+typedef struct {
+    const float* cos_table;
+    const float* sin_table;
+    int32_t max_positions;
+    int32_t style;
+} sa_rope;
+
+/*
+ * sa_decode_attention_append with the rotary embedding fused in: q and k_new
+ * are taken unrotated and rotated at each sequence's position L-1; the
+ * rotated key (and the unrotated v_new) are appended, and the attention uses
+ * the rotated query.  The cache then holds rotated keys, as a model with
+ * rotary embedding keeps it.  rope must be non-null and valid
+ * (SA_ERR_INVALID_ARG otherwise); not available with SA_VARIANT_VALU.
+ */
+int sa_decode_attention_append_rope(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
+                                    sa_bf16* k_cache, sa_bf16* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const float* sinks, int32_t window, const sa_rope* rope,
+                                    sa_bf16* out, const sa_dims* dims, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
  * Split-K partials only, for a caller that merges them itself (for example
  * across devices that each hold part of a context).  With S =
  * sa_decode_num_splits(dims, window), partition j of (b, h) covers attended

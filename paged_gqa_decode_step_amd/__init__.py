@@ -47,6 +47,19 @@ class Dims(ctypes.Structure):
     ]
 
 
+ROPE_HALF = 0
+ROPE_INTERLEAVED = 1
+
+
+class Rope(ctypes.Structure):
+    _fields_ = [
+        ("cos_table", ctypes.c_void_p),
+        ("sin_table", ctypes.c_void_p),
+        ("max_positions", ctypes.c_int32),
+        ("style", ctypes.c_int32),
+    ]
+
+
 class SAError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -55,7 +68,8 @@ class SAError(RuntimeError):
 
 _lib = None
 EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
-           "sa_decode_attention", "sa_decode_attention_append", "sa_decode_partials",
+           "sa_decode_attention", "sa_decode_attention_append",
+           "sa_decode_attention_append_rope", "sa_decode_partials",
            "sa_combine", "sa_read_bandwidth_probe", "sa_status_string")
 
 
@@ -82,6 +96,9 @@ def load(path: Optional[str] = None):
     lib.sa_decode_attention_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, dp, vp,
                                                sz, vp]
     lib.sa_decode_attention_append.restype = ctypes.c_int
+    lib.sa_decode_attention_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                    ctypes.POINTER(Rope), vp, dp, vp, sz, vp]
+    lib.sa_decode_attention_append_rope.restype = ctypes.c_int
     lib.sa_decode_partials.argtypes = [vp, vp, vp, vp, vp, i32, vp, vp, dp, vp]
     lib.sa_decode_partials.restype = ctypes.c_int
     lib.sa_combine.argtypes = [vp, vp, vp, i32, vp, dp, vp]
@@ -264,6 +281,47 @@ def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_
         _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d), _ptr(workspace),
         ws_bytes, _stream(stream))
     _raise(st, "sa_decode_attention_append")
+    return out
+
+
+def decode_attention_append_rope(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                 cos_table, sin_table, style=ROPE_HALF, sinks=None, window=0,
+                                 out=None, workspace=None, num_splits=0, variant=VARIANT_DEFAULT,
+                                 stream=None):
+    """The fused decode step with the rotary embedding of q and k_new at each
+    sequence's position L-1 (tables fp32 [positions][D/2]).  Returns ``out``."""
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    dev = q.device
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check(k_new, "k_new", torch.bfloat16, 3, dev)
+    _check(v_new, "v_new", torch.bfloat16, 3, dev)
+    if tuple(k_new.shape) != (d.num_seqs, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    for t, nm in ((cos_table, "cos_table"), (sin_table, "sin_table")):
+        _check(t, nm, torch.float32, 2, dev)
+        if t.shape[1] != d.head_dim // 2:
+            raise ValueError(f"{nm} must be [positions][head_dim/2]")
+    if cos_table.shape != sin_table.shape:
+        raise ValueError("cos_table and sin_table must have the same shape")
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != d.num_q_heads:
+            raise ValueError("sinks must have one entry per query head")
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, 3, dev)
+        if out.shape != q.shape:
+            raise ValueError("out must have the shape of q")
+    if workspace is None:
+        workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    r = Rope(cos_table.data_ptr(), sin_table.data_ptr(), cos_table.shape[0], int(style))
+    st = load().sa_decode_attention_append_rope(
+        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+        _ptr(seq_lens), _ptr(sinks), int(window), ctypes.byref(r), _ptr(out), ctypes.byref(d),
+        _ptr(workspace), ws_bytes, _stream(stream))
+    _raise(st, "sa_decode_attention_append_rope")
     return out
 
 

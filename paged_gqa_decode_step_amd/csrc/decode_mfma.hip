@@ -18,7 +18,7 @@ namespace {
 
 using namespace mfma;
 
-template <int BSL>
+template <int BSL, bool ROPE>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
     const int c16 = lane & 15;
@@ -50,11 +50,12 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int t1 = min(n, t0 + P);
 
     u32x4_t qop0, qop1;
-    load_query(a, b, g, lane, qop0, qop1);
-    const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n));
+    const int pos = ROPE ? rope_row(a, L) : 0;
+    load_query<ROPE>(a, b, g, lane, qop0, qop1, pos);
+    const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n), pos);
     State st;
     st.reset();
-    attend<BSL>(u, t0, t1, qop0, qop1, st);
+    attend<BSL, ROPE>(a, u, t0, t1, qop0, qop1, st);
     const float l_tot = st.total();
 
     if (a.mode == kWriteOut) {
@@ -103,18 +104,23 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
 }
 
-}  // namespace
-
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream) {
+template <bool ROPE>
+hipError_t launch_static(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hkv * a.num_splits);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL(decode_mfma_kernel<3>, grid, dim3(64), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(decode_mfma_kernel<4>, grid, dim3(64), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL(decode_mfma_kernel<5>, grid, dim3(64), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL(decode_mfma_kernel<6>, grid, dim3(64), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, ROPE>), grid, dim3(64), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, ROPE>), grid, dim3(64), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, ROPE>), grid, dim3(64), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, ROPE>), grid, dim3(64), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream) {
+    return rope ? launch_static<true>(a, stream) : launch_static<false>(a, stream);
 }
 
 }  // namespace sa

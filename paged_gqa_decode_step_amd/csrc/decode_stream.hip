@@ -54,7 +54,7 @@ __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, 
 #define SA_STREAM_OCC 0
 #endif
 
-template <int BSL>
+template <int BSL, bool ROPE>
 __global__ __launch_bounds__(64)
 #if SA_STREAM_OCC > 0
 __attribute__((amdgpu_waves_per_eu(SA_STREAM_OCC, SA_STREAM_OCC)))
@@ -129,11 +129,12 @@ void decode_stream_kernel(const DecodeArgs a) {
         const int s0 = x - ustart, s1 = seg_end - ustart;
 
         u32x4_t qop0, qop1;
-        load_query(a, b, g, lane, qop0, qop1);
-        const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n));
+        const int pos = ROPE ? rope_row(a, L) : 0;
+        load_query<ROPE>(a, b, g, lane, qop0, qop1, pos);
+        const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n), pos);
         State st;
         st.reset();
-        attend<BSL>(u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1, st);
+        attend<BSL, ROPE>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1, st);
         const float l_tot = st.total();
         if (lane == 0) {
             int* seg = a.unit_seg + 2 * (b * a.Hkv + g);
@@ -244,19 +245,25 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, o);
 }
 
-}  // namespace
-
-hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream) {
+template <bool ROPE>
+hipError_t launch_stream_partitions(const DecodeArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)2 * a.B * sizeof(int);
     const dim3 grid(a.num_waves);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL(decode_stream_kernel<3>, grid, dim3(64), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL(decode_stream_kernel<4>, grid, dim3(64), lds, stream, a); break;
-        case 5: hipLaunchKernelGGL(decode_stream_kernel<5>, grid, dim3(64), lds, stream, a); break;
-        case 6: hipLaunchKernelGGL(decode_stream_kernel<6>, grid, dim3(64), lds, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_stream_kernel<3, ROPE>), grid, dim3(64), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_stream_kernel<4, ROPE>), grid, dim3(64), lds, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_stream_kernel<5, ROPE>), grid, dim3(64), lds, stream, a); break;
+        case 6: hipLaunchKernelGGL((decode_stream_kernel<6, ROPE>), grid, dim3(64), lds, stream, a); break;
         default: return hipErrorInvalidValue;
     }
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream) {
+    hipError_t e = rope ? launch_stream_partitions<true>(a, stream)
+                        : launch_stream_partitions<false>(a, stream);
     if (e != hipSuccess) return e;
     // segments per unit if lengths were equal; picks the combine's width
     const long long units = (long long)a.B * a.Hkv;

@@ -90,6 +90,23 @@ __device__ __forceinline__ unsigned pack_bf16(float lo, float hi) {
     return __builtin_bit_cast(unsigned, v);
 }
 
+// bf16 halves of a 32-bit word, widened exactly
+__device__ __forceinline__ float bf16_lo(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Rotary embedding of one pair (x1, x2) by the angle with cosine c and sine s:
+// (x1 c - x2 s, x2 c + x1 s), each product and each sum rounded to float32 on
+// its own (no fused multiply-add), so the bf16 rounding that follows takes
+// the same decision wherever it is computed.
+__device__ __forceinline__ float rot_first(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+    return x1 * c - x2 * s;
+}
+__device__ __forceinline__ float rot_second(float x1, float x2, float c, float s) {
+#pragma clang fp contract(off)
+    return x2 * c + x1 * s;
+}
+
 __device__ __forceinline__ f32x4_t mfma(u32x4_t a, u32x4_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -135,6 +152,7 @@ struct Unit {
     // (k_new / v_new of this unit; q when nothing is appended, so that the
     // rows can be read unconditionally) and where the pools are written
     int new_slot;
+    int rope_pos;            // position of the new token in the rotary tables
     const uint16_t* kn_row;
     const uint16_t* vn_row;
     char* kstore;            // writable K pool + g * (bs*D*2)
@@ -160,7 +178,7 @@ __device__ __forceinline__ int new_token_slot(const DecodeArgs& a, int L, int n)
 }
 
 __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int lane,
-                                          int new_slot = -1) {
+                                          int new_slot = -1, int rope_pos = 0) {
     Unit u;
     const int bs = 1 << a.bs_log2;
     u.c16 = lane & 15;
@@ -176,6 +194,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.v_lane = (unsigned)(u.c16 * bs) * 2;
     u.scale_log2 = a.scale_log2;
     u.new_slot = new_slot;
+    u.rope_pos = rope_pos;
     const size_t row = ((size_t)b * a.Hkv + g) * kHeadDim;
     u.kn_row = a.k_new ? a.k_new + row : a.q;
     u.vn_row = a.k_new ? a.v_new + row : a.q;
@@ -186,8 +205,20 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
 
 // Query operand of head g*G + c16 (zero for c16 >= G): dims 8*q4..+7 and
 // 32+8*q4..+7.
+// Row of the rotary tables for a sequence of length L (> 0): position L-1,
+// past the tables' last row their last row.
+__device__ __forceinline__ int rope_row(const DecodeArgs& a, int L) {
+    return min(L - 1, a.rope_max_pos - 1);
+}
+
+// The query operands of a unit: lane (c16, q4) holds head g*G + c16, dims
+// 8q4..8q4+7 (qop0) and 32+8q4..32+8q4+7 (qop1); zero for c16 >= G.  With
+// ROPE they are rotated at table row `pos`.  Both pairings keep each pair
+// inside one lane: "half" pairs dim i with i+32, i.e. element e of qop0 with
+// element e of qop1; "interleaved" pairs the two halves of each 32-bit word.
+template <bool ROPE>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, int lane,
-                                           u32x4_t& qop0, u32x4_t& qop1) {
+                                           u32x4_t& qop0, u32x4_t& qop1, int pos = 0) {
     const int c16 = lane & 15, q4 = lane >> 4;
     qop0 = u32x4_t{0u, 0u, 0u, 0u};
     qop1 = u32x4_t{0u, 0u, 0u, 0u};
@@ -195,6 +226,40 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, in
         const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * a.G + c16) * kHeadDim + 8 * q4;
         qop0 = *reinterpret_cast<const u32x4_t*>(qp);
         qop1 = *reinterpret_cast<const u32x4_t*>(qp + 32);
+    }
+    if (!ROPE) return;
+    const float* cr = a.rope_cos + (size_t)pos * (kHeadDim / 2);
+    const float* sr = a.rope_sin + (size_t)pos * (kHeadDim / 2);
+    if (a.rope_style == kRopeHalf) {
+        // pair i = 8q4 + e: x1 = element e of qop0, x2 = element e of qop1
+        const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cr + 8 * q4);
+        const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cr + 8 * q4 + 4);
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sr + 8 * q4);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sr + 8 * q4 + 4);
+        const float c[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+        const float sn[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float a1 = bf16_lo(qop0[w]), b1 = bf16_hi(qop0[w]);   // x1 of pairs 2w, 2w+1
+            const float a2 = bf16_lo(qop1[w]), b2 = bf16_hi(qop1[w]);   // their x2
+            qop0[w] = pack_bf16(rot_first(a1, a2, c[2 * w], sn[2 * w]),
+                                rot_first(b1, b2, c[2 * w + 1], sn[2 * w + 1]));
+            qop1[w] = pack_bf16(rot_second(a1, a2, c[2 * w], sn[2 * w]),
+                                rot_second(b1, b2, c[2 * w + 1], sn[2 * w + 1]));
+        }
+    } else {
+        // pair i = 4q4 + w (qop0 word w) and 16 + 4q4 + w (qop1 word w)
+        const f32x4_t c0 = *reinterpret_cast<const f32x4_t*>(cr + 4 * q4);
+        const f32x4_t c1 = *reinterpret_cast<const f32x4_t*>(cr + 16 + 4 * q4);
+        const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sr + 4 * q4);
+        const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sr + 16 + 4 * q4);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float x1 = bf16_lo(qop0[w]), x2 = bf16_hi(qop0[w]);
+            qop0[w] = pack_bf16(rot_first(x1, x2, c0[w], s0[w]), rot_second(x1, x2, c0[w], s0[w]));
+            const float y1 = bf16_lo(qop1[w]), y2 = bf16_hi(qop1[w]);
+            qop1[w] = pack_bf16(rot_first(y1, y2, c1[w], s1[w]), rot_second(y1, y2, c1[w], s1[w]));
+        }
     }
 }
 
@@ -210,9 +275,10 @@ __device__ __forceinline__ int table_slice(const Unit& u, int blk0, int lane) {
 // the run spanning at most kMaxTableSlice blocks, whose table entries tbl
 // holds), folding into st.  kword / vval: this lane's word (lane & 31) of the
 // new token's K row and its element `lane` of the V row.
-template <int BSL>
+template <int BSL, bool ROPE>
 __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl,
-                                           unsigned kword, uint16_t vval, u32x4_t qop0,
+                                           unsigned kword, uint16_t vval, float2 kcos,
+                                           float2 ksin, int rope_style, u32x4_t qop0,
                                            u32x4_t qop1, State& st) {
     const int c16 = u.c16, q4 = u.q4;
     constexpr int bs = 1 << BSL;
@@ -317,11 +383,29 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         const int lane = c16 + 16 * q4;
         const unsigned noff = (unsigned)(u.new_slot & (bs - 1));
         const size_t blk_off = (size_t)nblk_id * u.blk_stride;
+        unsigned kw = kword;
+        if (ROPE) {
+            // the new key rotated at its position: word (lane & 31) holds dims
+            // 2w, 2w+1; with "half" pairing their partners are word w ^ 16
+            const unsigned other =
+                (unsigned)__builtin_amdgcn_ds_bpermute((lane ^ 16) << 2, (int)kword);
+            const float lo = bf16_lo(kword), hi = bf16_hi(kword);
+            if (rope_style == kRopeHalf) {
+                const float plo = bf16_lo(other), phi = bf16_hi(other);
+                kw = (lane & 16) == 0
+                         ? pack_bf16(rot_first(lo, plo, kcos.x, ksin.x),
+                                     rot_first(hi, phi, kcos.y, ksin.y))
+                         : pack_bf16(rot_second(plo, lo, kcos.x, ksin.x),
+                                     rot_second(phi, hi, kcos.y, ksin.y));
+            } else {
+                kw = pack_bf16(rot_first(lo, hi, kcos.x, ksin.x), rot_second(lo, hi, kcos.x, ksin.x));
+            }
+        }
         // V column: lane = dim.  K row: word (lane & 31) of the 128-byte row
         // (the upper half-wave stores the same words again).
         *reinterpret_cast<uint16_t*>(u.vstore + blk_off + ((unsigned)lane * bs + noff) * 2) = vval;
         *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
-            kword;
+            kw;
     };
     const bool new_first = has_new && u.new_slot < t0 + kStepTokens;
     if (new_first) store_new();
@@ -358,17 +442,31 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
 // blocks (t0 a multiple of 32).  The first run's table slice and the new
 // token's words are read here, with no branch, so they travel with the
 // caller's query loads.
-template <int BSL>
-__device__ __forceinline__ void attend(const Unit& u, int t0, int t1, u32x4_t qop0,
-                                       u32x4_t qop1, State& st) {
+template <int BSL, bool ROPE>
+__device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t0, int t1,
+                                       u32x4_t qop0, u32x4_t qop1, State& st) {
     constexpr int run = kMaxTableSlice << BSL;
     const int lane = u.c16 + 16 * u.q4;
     int tbl = table_slice(u, t0 >> BSL, lane);
     const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
     const uint16_t vval = u.vn_row[lane];
+    // cos / sin of the pairs of this lane's new-key word (read with no branch)
+    float2 kcos = {1.f, 1.f}, ksin = {0.f, 0.f};
+    if (ROPE) {
+        const size_t row = (size_t)u.rope_pos * (kHeadDim / 2);
+        const int w = lane & 31;
+        if (a.rope_style == kRopeHalf) {          // pairs 2(w & 15), 2(w & 15) + 1
+            kcos = *reinterpret_cast<const float2*>(a.rope_cos + row + 2 * (w & 15));
+            ksin = *reinterpret_cast<const float2*>(a.rope_sin + row + 2 * (w & 15));
+        } else {                                  // pair w
+            kcos.x = a.rope_cos[row + w];
+            ksin.x = a.rope_sin[row + w];
+        }
+    }
     for (int r0 = t0;;) {
         const int r1 = min(t1, r0 + run);
-        attend_run<BSL>(u, r0, r1, tbl, kword, vval, qop0, qop1, st);
+        attend_run<BSL, ROPE>(u, r0, r1, tbl, kword, vval, kcos, ksin, a.rope_style, qop0, qop1,
+                              st);
         if (r1 >= t1) break;
         r0 = r1;
         tbl = table_slice(u, r0 >> BSL, lane);

@@ -236,19 +236,27 @@ namespace {
 // Attention, and with k_new/v_new the KV append in the same launch.
 int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
            const sa_bf16* k_cache, const sa_bf16* v_cache, const int32_t* block_table,
-           const int32_t* seq_lens, const float* sinks, int32_t window, sa_bf16* out,
-           const sa_dims* dims, void* workspace, size_t workspace_bytes, void* stream) {
+           const int32_t* seq_lens, const float* sinks, int32_t window, const sa_rope* rope,
+           sa_bf16* out, const sa_dims* dims, void* workspace, size_t workspace_bytes,
+           void* stream) {
     int st = check_dims(dims, window);
     if (st != SA_OK) return st;
     if (dims->num_seqs == 0) return SA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
+        return SA_ERR_INVALID_ARG;
+    if (rope && (!rope->cos_table || !rope->sin_table || rope->max_positions < 1 ||
+                 (rope->style != SA_ROPE_HALF && rope->style != SA_ROPE_INTERLEAVED) || !k_new))
         return SA_ERR_INVALID_ARG;
     const bool valu = dims->variant == SA_VARIANT_VALU;
     if (valu && (dims->num_q_heads / dims->num_kv_heads > 8 || k_new)) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
     const Mode mode = choose_mode(dims, window, p);
-    auto launch_static = valu ? sa::launch_decode_valu : sa::launch_decode_mfma;
+    const bool with_rope = rope != nullptr;
+    auto launch_static = [valu, with_rope](const sa::DecodeArgs& args, hipStream_t strm) {
+        return valu ? sa::launch_decode_valu(args, strm)
+                    : sa::launch_decode_mfma(args, with_rope, strm);
+    };
     const WorkspaceLayout wl = workspace_layout(dims, window, p, mode);
     if (wl.total && (!workspace || workspace_bytes < wl.total)) return SA_ERR_WORKSPACE;
 
@@ -266,6 +274,12 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
         a.k_store = const_cast<uint16_t*>(k_cache);
         a.v_store = const_cast<uint16_t*>(v_cache);
     }
+    if (rope) {
+        a.rope_cos = rope->cos_table;
+        a.rope_sin = rope->sin_table;
+        a.rope_max_pos = rope->max_positions;
+        a.rope_style = rope->style == SA_ROPE_HALF ? sa::kRopeHalf : sa::kRopeInterleaved;
+    }
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
     if (mode == Mode::kBalanced) {
@@ -273,7 +287,7 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
         a.part_lse = (float*)(ws + wl.part_lse);
         a.unit_seg = (int32_t*)(ws + wl.unit_seg);
         a.num_waves = (int32_t)stream_waves(dims, window);
-        return to_status(sa::launch_decode_stream(a, s));
+        return to_status(sa::launch_decode_stream(a, with_rope, s));
     }
     if (p.splits == 1) {
         a.mode = sa::kWriteOut;
@@ -284,7 +298,7 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     a.counters = (int32_t*)(ws + wl.counters);
     if (mode == Mode::kFused) {
         a.mode = sa::kFusedCombine;
-        return to_status(sa::launch_decode_mfma(a, s));
+        return to_status(sa::launch_decode_mfma(a, with_rope, s));
     }
     a.mode = sa::kWritePartials;
     st = to_status(launch_static(a, s));
@@ -310,7 +324,7 @@ int sa_decode_attention(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16*
                         const sa_dims* dims, void* workspace, size_t workspace_bytes,
                         void* stream) {
     return decode(q, nullptr, nullptr, k_cache, v_cache, block_table, seq_lens, sinks, window,
-                  out, dims, workspace, workspace_bytes, stream);
+                  nullptr, out, dims, workspace, workspace_bytes, stream);
 }
 
 int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
@@ -323,8 +337,22 @@ int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_
     if (st != SA_OK) return st;
     if (dims->num_seqs == 0) return SA_OK;
     if (!k_new || !v_new) return SA_ERR_INVALID_ARG;
-    return decode(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks, window, out,
-                  dims, workspace, workspace_bytes, stream);
+    return decode(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks, window,
+                  nullptr, out, dims, workspace, workspace_bytes, stream);
+}
+
+int sa_decode_attention_append_rope(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
+                                    sa_bf16* k_cache, sa_bf16* v_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    const float* sinks, int32_t window, const sa_rope* rope,
+                                    sa_bf16* out, const sa_dims* dims, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    const int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!k_new || !v_new || !rope) return SA_ERR_INVALID_ARG;
+    return decode(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks, window, rope,
+                  out, dims, workspace, workspace_bytes, stream);
 }
 
 int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* v_cache,
@@ -347,7 +375,7 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.mode = sa::kWritePartials;
-    return to_status(sa::launch_decode_mfma(a, (hipStream_t)stream));
+    return to_status(sa::launch_decode_mfma(a, false, (hipStream_t)stream));
 }
 
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,

@@ -52,7 +52,15 @@ struct DecodeArgs {
     int32_t part_tokens;      // P: slots per partition (multiple of 32 and of bs)
     int32_t mode;             // PartitionMode
     float scale_log2;         // log2(e) / sqrt(D)
+    // rotary embedding of q and k_new at position L-1 (kernels built with it)
+    const float* rope_cos;    // [rope_max_pos][D/2]
+    const float* rope_sin;
+    int32_t rope_max_pos;
+    int32_t rope_style;       // kRopeHalf or kRopeInterleaved
 };
+
+constexpr int kRopeHalf = 0;          // pairs (i, i + D/2)
+constexpr int kRopeInterleaved = 1;   // pairs (2i, 2i + 1)
 
 struct CombineArgs {
     const float* part_o;
@@ -63,8 +71,9 @@ struct CombineArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_stream(const DecodeArgs& a, hipStream_t stream);
+// rope: the kernels built with the rotary embedding of q and k_new
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream);
+hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* data, size_t bytes, unsigned* sink, hipStream_t stream);

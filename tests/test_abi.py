@@ -40,7 +40,7 @@ def good_dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
     assert set(names) == set(sa.EXPORTS)
@@ -161,3 +161,25 @@ def test_read_probe_validates(lib):
     assert lib.sa_read_bandwidth_probe(None, 16, sink, None) == SA_ERR_INVALID_ARG
     assert lib.sa_read_bandwidth_probe(FAKE, 20, sink, None) == SA_ERR_INVALID_ARG
     assert lib.sa_read_bandwidth_probe(FAKE, 0, sink, None) == 0     # nothing launched
+
+
+def test_rope_entry_validates(lib):
+    d = good_dims()
+    good = sa.Rope(0x30000, 0x40000, 16, 0)
+    bad = [sa.Rope(None, 0x40000, 16, 0), sa.Rope(0x30000, None, 16, 0), sa.Rope(0x30000, 0x40000, 0, 0),
+           sa.Rope(0x30000, 0x40000, 16, 2)]
+    for r in bad:
+        assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, ctypes.byref(r), FAKE,
+                                                   ctypes.byref(d), FAKE, 1 << 30,
+                                                   None) == SA_ERR_INVALID_ARG
+    assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, None, FAKE, ctypes.byref(d),
+                                               FAKE, 1 << 30, None) == SA_ERR_INVALID_ARG
+    args = [FAKE] * 8
+    args[1] = None                                    # no k_new
+    assert lib.sa_decode_attention_append_rope(*args, 0, ctypes.byref(good), FAKE,
+                                               ctypes.byref(d), FAKE, 1 << 30,
+                                               None) == SA_ERR_INVALID_ARG
+    dv = good_dims(variant=3)
+    assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, ctypes.byref(good), FAKE,
+                                               ctypes.byref(dv), FAKE, 1 << 30,
+                                               None) == SA_ERR_UNSUPPORTED
