@@ -15,7 +15,8 @@ computes. It exists to check the HIP library, never to stand in for it:
   of the named concept; every such reading is listed in the design doc.
 
 ``oracle.rope`` adds the decode step with the rotary position embedding of
-the new token's query and key (page 1 lists RoPE as one fused kernel).
+the new token's query and key (page 1 lists RoPE as one fused kernel), and
+``oracle.multi_token`` the step with T > 1 causal query tokens per sequence.
 
 Pins (tests/test_oracle_*.py, ``-m "not gpu"``): a pure-Python brute force
 over a layout-free history, torch's fp64 ``scaled_dot_product_attention``
@@ -36,3 +37,4 @@ from .decode_step import (  # noqa: F401
     kv_append,
 )
 from . import rope  # noqa: F401,E402
+from . import multi_token  # noqa: F401,E402
