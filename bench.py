@@ -344,6 +344,63 @@ def rope_step_config(sa, torch, timer, dev, steps, warmup, variant, with_oracle=
     return e
 
 
+def tile_step_config(sa, torch, timer, dev, steps, warmup, variant, T=2, with_oracle=True):
+    """Speculative verify / chunked prefill on the batch-64 ragged paged layer:
+    T causal query tokens per sequence (T x 8 heads fill the 16 MFMA columns),
+    their K/V appended inside the launch, beside the one-token call on the same
+    cache."""
+    import synth
+    c = synth.CONFIGS["batch64_ragged"]
+    lens = synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + T
+    L = synth.make_layer(batch=c["batch"], q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                         lens=lens, seed=c["seed"] + 70, device=dev)
+    g = torch.Generator(device=dev).manual_seed(c["seed"] + 71)
+    B = c["batch"]
+    q = torch.randn(B, T, 64, 64, generator=g, device=dev).to(torch.bfloat16)
+    kn = torch.randn(B, T, 8, 64, generator=g, device=dev).to(torch.bfloat16)
+    vn = torch.randn(B, T, 8, 64, generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    out1 = torch.empty_like(L.q)
+    ws = sa.new_workspace(q, L.k_cache, L.v_cache, L.block_table, 0, variant=variant)
+    ws1 = sa.new_workspace(L.q, L.k_cache, L.v_cache, L.block_table, 0, variant=variant)
+
+    def tile(_=0):
+        sa.decode_attention_append(q, kn, vn, L.k_cache, L.v_cache, L.block_table, L.seq_lens,
+                                   L.sinks, 0, out=out, workspace=ws, variant=variant)
+
+    def one(_=0):
+        sa.decode_attention_append(L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                                   L.seq_lens, L.sinks, 0, out=out1, workspace=ws1,
+                                   variant=variant)
+    nbytes = (attn_bytes(lens.tolist(), 0) + B * 64 * 64 * 2 * 2 * (T - 1) +
+              append_bytes(B) * T)
+    timer.settle(one, warmup)
+    us_one = timer.mean_us(one, steps)
+    timer.settle(tile, warmup)
+    us = timer.mean_us(tile, steps)
+    e = entry(f"batch64_ragged, {T}-token query tile",
+              f"one call: append of {T} rows per sequence and causal attention of {T} query "
+              "tokens (paged full layer)", us, nbytes, us_one_token=round(us_one, 2),
+              tokens_per_s=round(B * T / (us * 1e-6), 1))
+    if with_oracle:
+        import oracle
+        h = host_inputs(L)
+        qb, knb, vnb = synth.to_bits(q), synth.to_bits(kn), synth.to_bits(vn)
+        with one_blas_thread():
+            t0 = time.perf_counter()
+            k2, v2 = oracle.multi_token.kv_append_multi(h["k"], h["v"], knb, vnb, h["bt"],
+                                                         h["lens"], 0)
+            oracle.multi_token.decode_attention_multi(qb, k2, v2, h["bt"], h["lens"], h["sinks"],
+                                                      0)
+            cpu_s = time.perf_counter() - t0
+        e.update(oracle_s=round(cpu_s, 4), oracle_gbps=round(nbytes / cpu_s / 1e9, 4),
+                 oracle_sample="the whole call, once; NumPy fp64, 1 thread",
+                 gpu_speedup_vs_oracle=round(cpu_s / (us * 1e-6), 1))
+    del L, q, kn, vn, out, out1, ws, ws1
+    torch.cuda.empty_cache()
+    return e
+
+
 def add_oracle(e, host):
     """Time the oracle on the saved host inputs and add it to the entry."""
     h, scale, reps = host
@@ -590,6 +647,12 @@ def main():
         hosts.append(None)
         print(f"# RoPE step: {rs['us']} us ({rs['us_without_rope']} without), {rs['gbps']} GB/s",
               flush=True)
+        ts = tile_step_config(sa, torch, timer, dev, args.steps, args.warmup, args.variant,
+                              with_oracle=oc)
+        configs.append(ts)
+        hosts.append(None)
+        print(f"# 2-token tile: {ts['us']} us ({ts['us_one_token']} for one token), "
+              f"{ts['gbps']} GB/s", flush=True)
         loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
                                   with_oracle=oc, fused=not args.separate_append)
         configs.append(loop)

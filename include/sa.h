@@ -74,6 +74,15 @@ typedef struct sa_dims {
                                     > 0: use at most this many split-K
                                     partitions per (sequence, KV head)         */
     int32_t variant;             /* 0: default kernels; see SA_VARIANT_*        */
+    int32_t num_query_tokens;    /* T: new tokens per sequence (0 means 1).  With
+                                    T > 1 (a query tile: speculative verify,
+                                    chunked prefill) token t sits at position
+                                    L-T+t and attends causally up to itself;
+                                    q / out are [B][T][Hq][D], k_new / v_new
+                                    [B][T][Hkv][D], partials [B][T][Hq][S][D].
+                                    Needs window <= 0 and T*(Hq/Hkv) <= 16
+                                    (SA_ERR_UNSUPPORTED otherwise); not with
+                                    RoPE or SA_VARIANT_VALU.                   */
 } sa_dims;
 
 enum {

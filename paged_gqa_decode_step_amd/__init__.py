@@ -44,6 +44,7 @@ class Dims(ctypes.Structure):
         ("num_blocks", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("variant", ctypes.c_int32),
+        ("num_query_tokens", ctypes.c_int32),
     ]
 
 
@@ -157,16 +158,32 @@ def _cache_dims(k_cache, v_cache, block_table, B, num_splits, variant):
                          f"got {tuple(v_cache.shape)}")
     if block_table.shape[0] != B:
         raise ValueError("block_table must have one row per sequence")
-    return Dims(B, 0, Hkv, D, bs, block_table.shape[1], NB, int(num_splits), int(variant))
+    return Dims(B, 0, Hkv, D, bs, block_table.shape[1], NB, int(num_splits), int(variant), 0)
 
 
 def dims_for(q, k_cache, v_cache, block_table, num_splits=0, variant=VARIANT_DEFAULT) -> Dims:
-    _check(q, "q", torch.bfloat16, 3)
+    """sa_dims for q ``[B][Hq][D]`` (one token per sequence) or ``[B][T][Hq][D]``
+    (T query tokens per sequence)."""
+    _check(q, "q", torch.bfloat16, 4 if isinstance(q, torch.Tensor) and q.dim() == 4 else 3)
     d = _cache_dims(k_cache, v_cache, block_table, q.shape[0], num_splits, variant)
-    d.num_q_heads = q.shape[1]
-    if q.shape[2] != d.head_dim:
+    if q.dim() == 4:
+        d.num_query_tokens = q.shape[1]
+    d.num_q_heads = q.shape[-2]
+    if q.shape[-1] != d.head_dim:
         raise ValueError("q and the caches disagree on head_dim")
     return d
+
+
+def _check_new_rows(k_new, v_new, d, dev):
+    """k_new / v_new: ``[B][Hkv][D]``, or ``[B][T][Hkv][D]`` with T query tokens."""
+    T = max(1, d.num_query_tokens)
+    nd = 4 if T > 1 or (isinstance(k_new, torch.Tensor) and k_new.dim() == 4) else 3
+    _check(k_new, "k_new", torch.bfloat16, nd, dev)
+    _check(v_new, "v_new", torch.bfloat16, nd, dev)
+    want = (d.num_seqs, d.num_kv_heads, d.head_dim) if nd == 3 else \
+        (d.num_seqs, T, d.num_kv_heads, d.head_dim)
+    if tuple(k_new.shape) != want or k_new.shape != v_new.shape:
+        raise ValueError(f"k_new / v_new must be {list(want)}")
 
 
 def _raise(st: int, what: str):
@@ -179,14 +196,17 @@ def _raise(st: int, what: str):
 # ---------------------------------------------------------------------------
 
 def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, window=0, stream=None):
-    """Write each sequence's new K/V row into its paged block or ring slot."""
-    _check(k_new, "k_new", torch.bfloat16, 3, k_cache.device)
-    _check(v_new, "v_new", torch.bfloat16, 3, k_cache.device)
+    """Write each sequence's new K/V rows into their paged blocks or ring slots:
+    ``[B][Hkv][D]`` (one token, position L-1) or ``[B][T][Hkv][D]`` (token t at
+    position L-T+t)."""
     _check(seq_lens, "seq_lens", torch.int32, 1, k_cache.device)
+    if not isinstance(k_new, torch.Tensor):
+        raise TypeError("k_new must be a torch.Tensor")
     B = k_new.shape[0]
     d = _cache_dims(k_cache, v_cache, block_table, B, 0, 0)
-    if tuple(k_new.shape) != (B, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
-        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if k_new.dim() == 4:
+        d.num_query_tokens = k_new.shape[1]
+    _check_new_rows(k_new, v_new, d, k_cache.device)
     if seq_lens.shape[0] != B:
         raise ValueError("seq_lens must have one entry per sequence")
     d.num_q_heads = d.num_kv_heads
@@ -238,7 +258,7 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, sinks=None, win
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 3, dev)
+        _check(out, "out", torch.bfloat16, q.dim(), dev)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
     if workspace is None:
@@ -259,10 +279,7 @@ def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_
     d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
     dev = q.device
     _check(seq_lens, "seq_lens", torch.int32, 1, dev)
-    _check(k_new, "k_new", torch.bfloat16, 3, dev)
-    _check(v_new, "v_new", torch.bfloat16, 3, dev)
-    if tuple(k_new.shape) != (d.num_seqs, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
-        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    _check_new_rows(k_new, v_new, d, dev)
     if sinks is not None:
         _check(sinks, "sinks", torch.float32, 1, dev)
         if sinks.shape[0] != d.num_q_heads:
@@ -270,7 +287,7 @@ def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 3, dev)
+        _check(out, "out", torch.bfloat16, q.dim(), dev)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
     if workspace is None:
@@ -293,10 +310,7 @@ def decode_attention_append_rope(q, k_new, v_new, k_cache, v_cache, block_table,
     d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
     dev = q.device
     _check(seq_lens, "seq_lens", torch.int32, 1, dev)
-    _check(k_new, "k_new", torch.bfloat16, 3, dev)
-    _check(v_new, "v_new", torch.bfloat16, 3, dev)
-    if tuple(k_new.shape) != (d.num_seqs, d.num_kv_heads, d.head_dim) or k_new.shape != v_new.shape:
-        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    _check_new_rows(k_new, v_new, d, dev)
     for t, nm in ((cos_table, "cos_table"), (sin_table, "sin_table")):
         _check(t, nm, torch.float32, 2, dev)
         if t.shape[1] != d.head_dim // 2:
@@ -310,7 +324,7 @@ def decode_attention_append_rope(q, k_new, v_new, k_cache, v_cache, block_table,
     if out is None:
         out = torch.empty_like(q)
     else:
-        _check(out, "out", torch.bfloat16, 3, dev)
+        _check(out, "out", torch.bfloat16, q.dim(), dev)
         if out.shape != q.shape:
             raise ValueError("out must have the shape of q")
     if workspace is None:
@@ -327,21 +341,22 @@ def decode_attention_append_rope(q, k_new, v_new, k_cache, v_cache, block_table,
 
 def decode_partials(q, k_cache, v_cache, block_table, seq_lens, window=0, num_splits=0,
                     part_o=None, part_lse=None, stream=None):
-    """Split-K partials ``(part_o [B][Hq][S][D], part_lse [B][Hq][S])`` without sink."""
+    """Split-K partials ``(part_o [B][Hq][S][D], part_lse [B][Hq][S])`` without sink
+    (with q ``[B][T][Hq][D]``: ``[B][T][Hq][S][D]`` and ``[B][T][Hq][S]``)."""
     d = dims_for(q, k_cache, v_cache, block_table, num_splits, VARIANT_DEFAULT)
     dev = q.device
     _check(seq_lens, "seq_lens", torch.int32, 1, dev)
     S = load().sa_decode_num_splits(ctypes.byref(d), int(window))
     _raise(min(S, 0), "sa_decode_num_splits")
-    B, Hq, D = q.shape
+    lead, D = tuple(q.shape[:-1]), q.shape[-1]
     if part_o is None:
-        part_o = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+        part_o = torch.empty(lead + (S, D), dtype=torch.float32, device=dev)
     if part_lse is None:
-        part_lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    _check(part_o, "part_o", torch.float32, 4, dev)
-    _check(part_lse, "part_lse", torch.float32, 3, dev)
-    if tuple(part_o.shape) != (B, Hq, S, D) or tuple(part_lse.shape) != (B, Hq, S):
-        raise ValueError(f"partials must be [B][Hq][{S}][D] and [B][Hq][{S}]")
+        part_lse = torch.empty(lead + (S,), dtype=torch.float32, device=dev)
+    _check(part_o, "part_o", torch.float32, len(lead) + 2, dev)
+    _check(part_lse, "part_lse", torch.float32, len(lead) + 1, dev)
+    if tuple(part_o.shape) != lead + (S, D) or tuple(part_lse.shape) != lead + (S,):
+        raise ValueError(f"partials must be {list(lead)}+[{S}][D] and {list(lead)}+[{S}]")
     st = load().sa_decode_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
                                    _ptr(seq_lens), int(window), _ptr(part_o), _ptr(part_lse),
                                    ctypes.byref(d), _stream(stream))
@@ -350,7 +365,18 @@ def decode_partials(q, k_cache, v_cache, block_table, seq_lens, window=0, num_sp
 
 
 def combine(part_o, part_lse, sinks=None, out=None, stream=None):
-    """Log-sum-exp combine of ``[B][Hq][S][D]`` partials with the sink."""
+    """Log-sum-exp combine of ``[B][Hq][S][D]`` (or ``[B][T][Hq][S][D]``)
+    partials with the sink; returns ``[B][Hq][D]`` (or ``[B][T][Hq][D]``)."""
+    if isinstance(part_o, torch.Tensor) and part_o.dim() == 5:      # rows (b*T + t)*Hq + h
+        B, T, Hq, S, D = part_o.shape
+        if out is not None:
+            _check(out, "out", torch.bfloat16, 4, part_o.device)
+            if tuple(out.shape) != (B, T, Hq, D):
+                raise ValueError("out must be [B][T][Hq][D]")
+        _check(part_lse, "part_lse", torch.float32, 4, part_o.device)
+        res = combine(part_o.view(B * T, Hq, S, D), part_lse.view(B * T, Hq, S), sinks,
+                      None if out is None else out.view(B * T, Hq, D), stream)
+        return res.view(B, T, Hq, D)
     _check(part_o, "part_o", torch.float32, 4)
     dev = part_o.device
     _check(part_lse, "part_lse", torch.float32, 3, dev)
@@ -364,7 +390,7 @@ def combine(part_o, part_lse, sinks=None, out=None, stream=None):
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, 3, dev)
-    d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0)
+    d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0, 0)
     st = load().sa_combine(_ptr(part_o), _ptr(part_lse), _ptr(sinks), int(S), _ptr(out),
                            ctypes.byref(d), _stream(stream))
     _raise(st, "sa_combine")

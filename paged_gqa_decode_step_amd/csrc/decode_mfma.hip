@@ -18,7 +18,7 @@ namespace {
 
 using namespace mfma;
 
-template <int BSL, bool ROPE>
+template <int BSL, bool ROPE, bool MULTI>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
     const int c16 = lane & 15;
@@ -28,8 +28,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int bg = blockIdx.x - split * units;     // leave early, late ids
     const int b = bg / a.Hkv;
     const int g = bg - b * a.Hkv;
-    const int h = g * a.G + c16;
-    const bool head_ok = c16 < a.G;
+    const Col col = column(a, lane);
+    const bool head_ok = col.ok;
 
     const int L = a.seq_lens[b];
     int n = L;
@@ -37,7 +37,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     n = max(0, min(n, a.mbs << a.bs_log2));
     const int P = a.part_tokens;
     const int t0 = split * P;
-    const size_t bh = (size_t)b * a.Hq + h;
+    const size_t bh = col_row(a, b, g, col);       // this lane's (token, head) row
 
     if (t0 >= n) {
         if (a.mode == kWritePartials) {
@@ -52,10 +52,10 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     u32x4_t qop0, qop1;
     const int pos = ROPE ? rope_row(a, L) : 0;
     load_query<ROPE>(a, b, g, lane, qop0, qop1, pos);
-    const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n), pos);
+    const Unit u = make_unit(a, b, g, lane, MULTI ? -1 : new_token_slot(a, L, n), pos, L);
     State st;
     st.reset();
-    attend<BSL, ROPE>(a, u, t0, t1, qop0, qop1, st);
+    attend<BSL, ROPE, MULTI>(a, u, t0, t1, qop0, qop1, st);
     const float l_tot = st.total();
 
     if (a.mode == kWriteOut) {
@@ -63,9 +63,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         return;
     }
     const int S = a.num_splits;
-    const size_t bh0 = (size_t)b * a.Hq + g * a.G;     // first head of the group
-    write_partial(a.G, lane, st, l_tot, a.part_o + (bh0 * S + split) * kHeadDim,
-                  (size_t)S * kHeadDim, a.part_lse + bh0 * S + split, (size_t)S);
+    write_partial(head_ok, bh, lane, st, l_tot, a.part_o + (size_t)split * kHeadDim,
+                  (size_t)S * kHeadDim, a.part_lse + split, (size_t)S);
     if (a.mode != kFusedCombine) return;
 
     // Fused combine: the last partition of (b, g) to finish merges them all.
@@ -80,7 +79,7 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     if (lane == 0) a.counters[bg] = 0;               // ready for the next call
     if (!head_ok) return;
 
-    const float sig = a.sinks ? a.sinks[h] : -INFINITY;   // natural log
+    const float sig = a.sinks ? a.sinks[g * a.G + col.h] : -INFINITY;   // natural log
     float M = sig;
     for (int j = 0; j < nparts; ++j) M = fmaxf(M, a.part_lse[bh * S + j]);
     f32x4_t num[4];
@@ -104,14 +103,14 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
 }
 
-template <bool ROPE>
+template <bool ROPE, bool MULTI>
 hipError_t launch_static(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hkv * a.num_splits);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, ROPE>), grid, dim3(64), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, ROPE>), grid, dim3(64), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, ROPE>), grid, dim3(64), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, ROPE>), grid, dim3(64), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
+        case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -120,7 +119,8 @@ hipError_t launch_static(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream) {
-    return rope ? launch_static<true>(a, stream) : launch_static<false>(a, stream);
+    if (a.T > 1) return rope ? hipErrorInvalidValue : launch_static<false, true>(a, stream);
+    return rope ? launch_static<true, false>(a, stream) : launch_static<false, false>(a, stream);
 }
 
 }  // namespace sa

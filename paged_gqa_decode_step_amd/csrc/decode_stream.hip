@@ -54,7 +54,7 @@ __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, 
 #define SA_STREAM_OCC 0
 #endif
 
-template <int BSL, bool ROPE>
+template <int BSL, bool ROPE, bool MULTI>
 __global__ __launch_bounds__(64)
 #if SA_STREAM_OCC > 0
 __attribute__((amdgpu_waves_per_eu(SA_STREAM_OCC, SA_STREAM_OCC)))
@@ -131,10 +131,11 @@ void decode_stream_kernel(const DecodeArgs a) {
         u32x4_t qop0, qop1;
         const int pos = ROPE ? rope_row(a, L) : 0;
         load_query<ROPE>(a, b, g, lane, qop0, qop1, pos);
-        const Unit u = make_unit(a, b, g, lane, new_token_slot(a, L, n), pos);
+        const Unit u = make_unit(a, b, g, lane, MULTI ? -1 : new_token_slot(a, L, n), pos, L);
         State st;
         st.reset();
-        attend<BSL, ROPE>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1, st);
+        attend<BSL, ROPE, MULTI>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1,
+                                 st);
         const float l_tot = st.total();
         if (lane == 0) {
             int* seg = a.unit_seg + 2 * (b * a.Hkv + g);
@@ -144,9 +145,11 @@ void decode_stream_kernel(const DecodeArgs a) {
         if (s0 == 0 && s1 == steps) {
             write_out(a, b, g, lane, st, l_tot);
         } else {
-            const size_t sl = (size_t)(2 * i + slot) * a.G;
-            write_partial(a.G, lane, st, l_tot, a.part_o + sl * kHeadDim, kHeadDim,
-                          a.part_lse + sl, 1);
+            // partial slot: T*G rows, one per (query token, head) column
+            const int ncol = a.T * a.G;
+            const size_t sl = (size_t)(2 * i + slot) * ncol;
+            write_partial((lane & 15) < ncol, lane & 15, lane, st, l_tot,
+                          a.part_o + sl * kHeadDim, kHeadDim, a.part_lse + sl, 1);
         }
         slot = 1;
         x = seg_end;
@@ -176,11 +179,14 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     __shared__ float s_max[WAVES];
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
-    const int bh = blockIdx.x;
-    const int b = bh / a.Hq;
-    const int h = bh - b * a.Hq;
+    const int bh = blockIdx.x;                  // out row (b*T + t)*Hq + h
+    const int bt = bh / a.Hq;
+    const int h = bh - bt * a.Hq;
+    const int b = bt / a.T;
+    const int tq = bt - b * a.T;
     const int g = h / a.G;
-    const int hl = h - g * a.G;
+    const int hl = tq * a.G + (h - g * a.G);    // column of (tq, h) in a partial slot
+    const int ncol = a.T * a.G;
     const int2 rec = *reinterpret_cast<const int2*>(a.unit_seg + 2 * (b * a.Hkv + g));
     // every unit's record is written by this call; the clamps only keep a
     // damaged one from reading past the partial slots
@@ -196,13 +202,16 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j) {
             const int k = min(k0 + j, nseg - 1);
-            const size_t sl = (size_t)(k == 0 ? first : 2 * (i0 + k)) * a.G + hl;
+            const size_t sl = (size_t)(k == 0 ? first : 2 * (i0 + k)) * ncol + hl;
             l[j] = a.part_lse[sl];
             o[j] = a.part_o[sl * kHeadDim + lane];
         }
         float M2 = M;
 #pragma unroll
         for (int j = 0; j < kCombineChunk; ++j) M2 = fmaxf(M2, k0 + j < nseg ? l[j] : -INFINITY);
+        // no segment with a slot for this column yet (several query tokens:
+        // segments before a token's position are empty): nothing to add
+        if (M2 == -INFINITY) continue;
         const float r = __builtin_amdgcn_exp2f((M - M2) * kLog2e);   // 0 while M = -inf
         float cn = 0.f, cd = 0.f;
 #pragma unroll
@@ -245,15 +254,15 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, o);
 }
 
-template <bool ROPE>
+template <bool ROPE, bool MULTI>
 hipError_t launch_stream_partitions(const DecodeArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)2 * a.B * sizeof(int);
     const dim3 grid(a.num_waves);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL((decode_stream_kernel<3, ROPE>), grid, dim3(64), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_stream_kernel<4, ROPE>), grid, dim3(64), lds, stream, a); break;
-        case 5: hipLaunchKernelGGL((decode_stream_kernel<5, ROPE>), grid, dim3(64), lds, stream, a); break;
-        case 6: hipLaunchKernelGGL((decode_stream_kernel<6, ROPE>), grid, dim3(64), lds, stream, a); break;
+        case 3: hipLaunchKernelGGL((decode_stream_kernel<3, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
+        case 4: hipLaunchKernelGGL((decode_stream_kernel<4, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
+        case 5: hipLaunchKernelGGL((decode_stream_kernel<5, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
+        case 6: hipLaunchKernelGGL((decode_stream_kernel<6, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -262,13 +271,15 @@ hipError_t launch_stream_partitions(const DecodeArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream) {
-    hipError_t e = rope ? launch_stream_partitions<true>(a, stream)
-                        : launch_stream_partitions<false>(a, stream);
+    hipError_t e = a.T > 1 ? (rope ? hipErrorInvalidValue
+                                   : launch_stream_partitions<false, true>(a, stream))
+                 : rope ? launch_stream_partitions<true, false>(a, stream)
+                        : launch_stream_partitions<false, false>(a, stream);
     if (e != hipSuccess) return e;
     // segments per unit if lengths were equal; picks the combine's width
     const long long units = (long long)a.B * a.Hkv;
     const long long per_unit = (a.num_waves + units - 1) / units + 1;
-    const dim3 cgrid((unsigned)a.B * a.Hq);
+    const dim3 cgrid((unsigned)a.B * a.T * a.Hq);
     if (per_unit <= kCombineChunk * 3 / 4)
         hipLaunchKernelGGL(combine_stream_kernel<1>, cgrid, dim3(64), 0, stream, a);
     else if (per_unit <= 64)

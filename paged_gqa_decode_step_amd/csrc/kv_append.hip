@@ -1,14 +1,17 @@
-// KV append: the new token's K and V go to its paged block or ring slot.
+// KV append: the new tokens' K and V go to their paged blocks or ring slots.
 //
 // SimpleLLM README, optimisation table: the fused decode-attention kernel
 // also performs the KV append; full-attention layers keep a paged cache and
-// sliding-window layers a ring buffer.  Position L-1 of sequence b lives in
-// slot L-1 (paged) or (L-1) mod W (ring); the slot's block comes from the
-// block table.  K rows are stored [bs][D] inside a block and V rows [D][bs].
+// sliding-window layers a ring buffer.  Position p of sequence b lives in
+// slot p (paged) or p mod W (ring); the slot's block comes from the block
+// table.  K rows are stored [bs][D] inside a block and V rows [D][bs].  With
+// T new tokens per sequence (a query tile; paged layers only) token t sits at
+// position L-T+t; one token is position L-1.
 //
-// One 64-lane wavefront per (sequence, KV head): lanes 0..7 store the 128-byte
-// K row as eight 16-byte stores; all 64 lanes store one 2-byte V element each
-// (the V column of the slot).  A bit copy; no arithmetic on the values.
+// One 64-lane wavefront per (sequence, KV head), token by token: lanes 0..7
+// store the 128-byte K row as eight 16-byte stores; all 64 lanes store one
+// 2-byte V element each (the V column of the slot).  A bit copy; no
+// arithmetic on the values.
 #include "sa_internal.h"
 
 namespace sa {
@@ -22,22 +25,26 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
     const int b = bg / a.Hkv;
     const int g = bg - b * a.Hkv;
     const int L = a.seq_lens[b];
-    if (L <= 0) return;
-    const int p = L - 1;
-    const int slot = a.window > 0 ? p % a.window : p;
-    const int j = slot >> a.bs_log2;
-    if (j >= a.mbs) return;                                  // beyond the table row
-    const int blk = a.block_table[(size_t)b * a.mbs + j];
-    if (blk < 0 || blk >= a.num_blocks) return;              // never write wild
     const int bs = 1 << a.bs_log2;
-    const int off = slot & (bs - 1);
-    const size_t head_base = ((size_t)blk * a.Hkv + g) * (size_t)(bs * kHeadDim);
-    const size_t src = ((size_t)b * a.Hkv + g) * kHeadDim;
-    if (lane < kHeadDim / 8) {
-        const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.k_new + src + lane * 8);
-        *reinterpret_cast<u32x4_t*>(a.k_cache + head_base + (size_t)off * kHeadDim + lane * 8) = k;
+    // new token t of the sequence sits at position L - T + t (one token: L - 1)
+    for (int t = 0; t < a.T; ++t) {
+        const int p = L - a.T + t;
+        if (p < 0) continue;
+        const int slot = a.window > 0 ? p % a.window : p;
+        const int j = slot >> a.bs_log2;
+        if (j >= a.mbs) continue;                                // beyond the table row
+        const int blk = a.block_table[(size_t)b * a.mbs + j];
+        if (blk < 0 || blk >= a.num_blocks) continue;            // never write wild
+        const int off = slot & (bs - 1);
+        const size_t head_base = ((size_t)blk * a.Hkv + g) * (size_t)(bs * kHeadDim);
+        const size_t src = (((size_t)b * a.T + t) * a.Hkv + g) * kHeadDim;
+        if (lane < kHeadDim / 8) {
+            const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.k_new + src + lane * 8);
+            *reinterpret_cast<u32x4_t*>(a.k_cache + head_base + (size_t)off * kHeadDim + lane * 8) =
+                k;
+        }
+        a.v_cache[head_base + (size_t)lane * bs + off] = a.v_new[src + lane];
     }
-    a.v_cache[head_base + (size_t)lane * bs + off] = a.v_new[src + lane];
 }
 
 }  // namespace

@@ -153,8 +153,11 @@ struct Unit {
     // rows can be read unconditionally) and where the pools are written
     int new_slot;
     int rope_pos;            // position of the new token in the rotary tables
-    const uint16_t* kn_row;
+    int L, T, G;             // sequence length; query tokens (new slots L-T..L-1); heads
+    bool appends;            // the launch appends (k_new given)
+    const uint16_t* kn_row;  // token 0's rows; token t's are kn_stride elements further
     const uint16_t* vn_row;
+    int kn_stride;
     char* kstore;            // writable K pool + g * (bs*D*2)
     char* vstore;
     const int32_t* bt_row;   // block table row of the sequence
@@ -178,7 +181,7 @@ __device__ __forceinline__ int new_token_slot(const DecodeArgs& a, int L, int n)
 }
 
 __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int lane,
-                                          int new_slot = -1, int rope_pos = 0) {
+                                          int new_slot = -1, int rope_pos = 0, int L = 0) {
     Unit u;
     const int bs = 1 << a.bs_log2;
     u.c16 = lane & 15;
@@ -195,7 +198,12 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.scale_log2 = a.scale_log2;
     u.new_slot = new_slot;
     u.rope_pos = rope_pos;
-    const size_t row = ((size_t)b * a.Hkv + g) * kHeadDim;
+    u.L = L;
+    u.T = a.T;
+    u.G = a.G;
+    u.kn_stride = a.Hkv * kHeadDim;
+    u.appends = a.k_new != nullptr;
+    const size_t row = ((size_t)b * a.T * a.Hkv + g) * kHeadDim;
     u.kn_row = a.k_new ? a.k_new + row : a.q;
     u.vn_row = a.k_new ? a.v_new + row : a.q;
     u.kstore = reinterpret_cast<char*>(a.k_store) + (size_t)g * bs * kHeadDim * 2;
@@ -205,6 +213,25 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
 
 // Query operand of head g*G + c16 (zero for c16 >= G): dims 8*q4..+7 and
 // 32+8*q4..+7.
+// The query column of a lane: c16 = t*G + h is query token t, head g*G + h of
+// the unit (one token: t = 0, h = c16); columns past T*G are idle.
+struct Col {
+    bool ok;
+    int t, h;
+};
+__device__ __forceinline__ Col column(const DecodeArgs& a, int lane) {
+    const int c16 = lane & 15;
+    Col c;
+    c.t = c16 / a.G;
+    c.h = c16 - c.t * a.G;
+    c.ok = c.t < a.T;
+    return c;
+}
+// q / out row of a column of unit (b, g)
+__device__ __forceinline__ size_t col_row(const DecodeArgs& a, int b, int g, const Col& c) {
+    return ((size_t)b * a.T + c.t) * a.Hq + g * a.G + c.h;
+}
+
 // Row of the rotary tables for a sequence of length L (> 0): position L-1,
 // past the tables' last row their last row.
 __device__ __forceinline__ int rope_row(const DecodeArgs& a, int L) {
@@ -219,11 +246,12 @@ __device__ __forceinline__ int rope_row(const DecodeArgs& a, int L) {
 template <bool ROPE>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, int lane,
                                            u32x4_t& qop0, u32x4_t& qop1, int pos = 0) {
-    const int c16 = lane & 15, q4 = lane >> 4;
+    const int q4 = lane >> 4;
     qop0 = u32x4_t{0u, 0u, 0u, 0u};
     qop1 = u32x4_t{0u, 0u, 0u, 0u};
-    if (c16 < a.G) {
-        const uint16_t* qp = a.q + ((size_t)b * a.Hq + g * a.G + c16) * kHeadDim + 8 * q4;
+    const Col c = column(a, lane);
+    if (c.ok) {
+        const uint16_t* qp = a.q + col_row(a, b, g, c) * kHeadDim + 8 * q4;
         qop0 = *reinterpret_cast<const u32x4_t*>(qp);
         qop1 = *reinterpret_cast<const u32x4_t*>(qp + 32);
     }
@@ -275,7 +303,7 @@ __device__ __forceinline__ int table_slice(const Unit& u, int blk0, int lane) {
 // the run spanning at most kMaxTableSlice blocks, whose table entries tbl
 // holds), folding into st.  kword / vval: this lane's word (lane & 31) of the
 // new token's K row and its element `lane` of the V row.
-template <int BSL, bool ROPE>
+template <int BSL, bool ROPE, bool MULTI>
 __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl,
                                            unsigned kword, uint16_t vval, float2 kcos,
                                            float2 ksin, int rope_style, u32x4_t qop0,
@@ -285,7 +313,9 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     const int blk0 = t0 >> BSL;
     const int last_chunk = (t1 - 1) & ~7;
     const int nsteps = (t1 - t0 + kStepTokens - 1) / kStepTokens;
-    const bool has_new = u.new_slot >= t0 && u.new_slot < t1;   // wave-uniform
+    const bool has_new = !MULTI && u.new_slot >= t0 && u.new_slot < t1;   // wave-uniform
+    // several query tokens: token t of a column sees slots below L - T + t + 1
+    const int col_lim = MULTI ? min(t1, u.L - u.T + c16 / u.G + 1) : t1;
     // block of the new slot (any lane when there is none: bpermute wraps),
     // outside the branch so the table wait is not merged into the join below
     const unsigned nblk_id =
@@ -327,11 +357,19 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
             t[4 + i] = s1[i] * u.scale_log2;
         }
         const int tok = t0 + (s << 5) + (q4 << 3);   // slot of t[0] on this lane
-        if (tok + 8 > t1) {                           // only in a run's last step
-            const int valid = max(0, min(8, t1 - tok));
+        if (MULTI && tok + 8 > col_lim) {             // the column's causal limit
+            const int valid = max(0, min(8, col_lim - tok));
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (e >= valid) t[e] = -INFINITY;
+        }
+        if (tok + 8 > t1) {                           // only in a run's last step
+            const int valid = max(0, min(8, t1 - tok));
+            if (!MULTI) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (e >= valid) t[e] = -INFINITY;
+            }
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 const unsigned mask = (2 * w < valid ? 0x0000FFFFu : 0u) |
@@ -409,6 +447,24 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     };
     const bool new_first = has_new && u.new_slot < t0 + kStepTokens;
     if (new_first) store_new();
+    if (MULTI && u.appends) {
+        // every new token whose slot lies in this run, before any load
+        for (int t = 0; t < u.T; ++t) {
+            const int slot = u.L - u.T + t;                  // wave-uniform
+            if (slot < t0 || slot >= t1) continue;
+            const int lane = c16 + 16 * q4;
+            const unsigned nb =
+                (unsigned)__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl);
+            const unsigned noff = (unsigned)(slot & (bs - 1));
+            const size_t off = (size_t)nb * u.blk_stride;
+            const unsigned kw =
+                reinterpret_cast<const unsigned*>(u.kn_row + (size_t)t * u.kn_stride)[lane & 31];
+            const uint16_t vv = (u.vn_row + (size_t)t * u.kn_stride)[lane];
+            *reinterpret_cast<uint16_t*>(u.vstore + off + ((unsigned)lane * bs + noff) * 2) = vv;
+            *reinterpret_cast<unsigned*>(u.kstore + off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
+                kw;
+        }
+    }
 
     // Two register sets in ping-pong: the loads of step s+1 are in flight
     // while step s computes.  The loop covers whole pairs that still have a
@@ -442,7 +498,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
 // blocks (t0 a multiple of 32).  The first run's table slice and the new
 // token's words are read here, with no branch, so they travel with the
 // caller's query loads.
-template <int BSL, bool ROPE>
+template <int BSL, bool ROPE, bool MULTI = false>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t0, int t1,
                                        u32x4_t qop0, u32x4_t qop1, State& st) {
     constexpr int run = kMaxTableSlice << BSL;
@@ -465,8 +521,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
     }
     for (int r0 = t0;;) {
         const int r1 = min(t1, r0 + run);
-        attend_run<BSL, ROPE>(u, r0, r1, tbl, kword, vval, kcos, ksin, a.rope_style, qop0, qop1,
-                              st);
+        attend_run<BSL, ROPE, MULTI>(u, r0, r1, tbl, kword, vval, kcos, ksin, a.rope_style, qop0,
+                                     qop1, st);
         if (r1 >= t1) break;
         r0 = r1;
         tbl = table_slice(u, r0 >> BSL, lane);
@@ -477,12 +533,12 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
 // out = acc / (l + e^(sigma - m)) (all in the log2 domain).
 __device__ __forceinline__ void write_out(const DecodeArgs& a, int b, int g, int lane,
                                           const State& st, float l_tot) {
-    const int c16 = lane & 15, q4 = lane >> 4;
-    if (c16 >= a.G) return;
-    const int h = g * a.G + c16;
-    const float sig = a.sinks ? a.sinks[h] * kLog2e : -INFINITY;
+    const int q4 = lane >> 4;
+    const Col c = column(a, lane);
+    if (!c.ok) return;
+    const float sig = a.sinks ? a.sinks[g * a.G + c.h] * kLog2e : -INFINITY;
     const float inv = 1.0f / (l_tot + __builtin_amdgcn_exp2f(sig - st.m));
-    uint16_t* op = a.out + ((size_t)b * a.Hq + h) * kHeadDim + 4 * q4;
+    uint16_t* op = a.out + col_row(a, b, g, c) * kHeadDim + 4 * q4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const u32x2_t o = {pack_bf16(st.acc[j][0] * inv, st.acc[j][1] * inv),
@@ -491,28 +547,34 @@ __device__ __forceinline__ void write_out(const DecodeArgs& a, int b, int g, int
     }
 }
 
-// zeros for the unit's heads (nothing attended: the sink has no value row)
+// zeros for the unit's columns (nothing attended: the sink has no value row)
 __device__ __forceinline__ void write_zero(const DecodeArgs& a, int b, int g, int lane) {
-    const int c16 = lane & 15, q4 = lane >> 4;
-    if (c16 >= a.G) return;
-    uint16_t* op = a.out + ((size_t)b * a.Hq + g * a.G + c16) * kHeadDim + 4 * q4;
+    const int q4 = lane >> 4;
+    const Col c = column(a, lane);
+    if (!c.ok) return;
+    uint16_t* op = a.out + col_row(a, b, g, c) * kHeadDim + 4 * q4;
     const u32x2_t z = {0u, 0u};
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x2_t*>(op + 16 * j) = z;
 }
 
-// Partial of a run: o = acc / l (fp32, row of 64 per head at po + head*64),
-// lse = ln sum e^s = (m + log2 l) ln 2 at pl[head].
-__device__ __forceinline__ void write_partial(int G, int lane, const State& st, float l_tot,
-                                              float* po, size_t head_stride, float* pl,
-                                              size_t lse_stride) {
-    const int c16 = lane & 15, q4 = lane >> 4;
-    if (c16 >= G) return;
-    const float inv = 1.0f / l_tot;
-    float* p = po + c16 * head_stride + 4 * q4;
+// Partial of a run for this lane's column (when ok): o = acc / l (fp32, 64
+// values at po + row*row_stride), lse = ln sum e^s = (m + log2 l) ln 2 at
+// pl[row * lse_stride].
+__device__ __forceinline__ void write_partial(bool ok, size_t row, int lane, const State& st,
+                                              float l_tot, float* po, size_t row_stride,
+                                              float* pl, size_t lse_stride) {
+    const int q4 = lane >> 4;
+    if (!ok) return;
+    // a column with no slot in the run (a query token before the run's slots:
+    // only with several query tokens) leaves o = 0 and lse = -inf, weight 0
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+    float* p = po + row * row_stride + 4 * q4;
 #pragma unroll
     for (int j = 0; j < 4; ++j) *reinterpret_cast<f32x4_t*>(p + 16 * j) = st.acc[j] * inv;
-    if (q4 == 0) pl[c16 * lse_stride] = (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
+    if (q4 == 0)
+        pl[row * lse_stride] = empty ? -INFINITY : (st.m + __builtin_amdgcn_logf(l_tot)) * kLn2;
 }
 
 }  // namespace mfma

@@ -45,15 +45,21 @@ int log2_exact(int x) {
     return (1 << l) == x ? l : -1;
 }
 
+// T: new tokens (query tokens) per sequence
+int query_tokens(const sa_dims* d) { return d->num_query_tokens > 0 ? d->num_query_tokens : 1; }
+
 int check_dims(const sa_dims* d, int32_t window) {
     if (!d) return SA_ERR_INVALID_ARG;
     if (d->num_seqs < 0 || d->num_q_heads < 1 || d->num_kv_heads < 1 ||
         d->max_blocks_per_seq < 1 || d->num_blocks < 1 || d->num_splits < 0 ||
-        d->head_dim < 1 || d->block_size < 1)
+        d->head_dim < 1 || d->block_size < 1 || d->num_query_tokens < 0)
         return SA_ERR_INVALID_ARG;
     if (d->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
     if (d->num_q_heads % d->num_kv_heads) return SA_ERR_UNSUPPORTED;
-    if (d->num_q_heads / d->num_kv_heads > sa::kMaxGroup) return SA_ERR_UNSUPPORTED;
+    // (query tokens) x (heads per KV head) columns fill one 16-column MFMA tile
+    if ((long long)query_tokens(d) * (d->num_q_heads / d->num_kv_heads) > sa::kMaxGroup)
+        return SA_ERR_UNSUPPORTED;
+    if (query_tokens(d) > 1 && window > 0) return SA_ERR_UNSUPPORTED;   // a W-slot ring
     const int l = log2_exact(d->block_size);
     if (l < 3 || l > 6) return SA_ERR_UNSUPPORTED;
     if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_MFMA_BALANCED)
@@ -149,13 +155,13 @@ WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p
     WorkspaceLayout w{};
     size_t rows, lse;        // partial rows of D floats, and lse entries
     if (m == Mode::kBalanced) {
-        const size_t slots = (size_t)stream_waves(d, window) * 2 *
+        const size_t slots = (size_t)stream_waves(d, window) * 2 * query_tokens(d) *
                              (d->num_q_heads / d->num_kv_heads);
         rows = slots;
         lse = slots;
     } else {
         if (p.splits <= 1) return w;
-        rows = (size_t)d->num_seqs * d->num_q_heads * p.splits;
+        rows = (size_t)d->num_seqs * query_tokens(d) * d->num_q_heads * p.splits;
         lse = rows;
     }
     w.counters = 0;
@@ -167,7 +173,8 @@ WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p
 }
 
 bool grid_fits(const sa_dims* d, int32_t splits) {
-    return (long long)d->num_seqs * d->num_kv_heads * splits < INT_MAX;
+    return (long long)d->num_seqs * d->num_kv_heads * splits < INT_MAX &&
+           (long long)d->num_seqs * query_tokens(d) * d->num_q_heads < INT_MAX;
 }
 
 sa::DecodeArgs decode_args(const sa_dims* d, int32_t window, const Plan& p) {
@@ -176,6 +183,7 @@ sa::DecodeArgs decode_args(const sa_dims* d, int32_t window, const Plan& p) {
     a.Hq = d->num_q_heads;
     a.Hkv = d->num_kv_heads;
     a.G = d->num_q_heads / d->num_kv_heads;
+    a.T = query_tokens(d);
     a.bs_log2 = log2_exact(d->block_size);
     a.mbs = d->max_blocks_per_seq;
     a.num_blocks = d->num_blocks;
@@ -214,6 +222,7 @@ int sa_kv_append(const sa_bf16* k_new, const sa_bf16* v_new, sa_bf16* k_cache,
     a.mbs = dims->max_blocks_per_seq;
     a.num_blocks = dims->num_blocks;
     a.window = window > 0 ? window : 0;
+    a.T = query_tokens(dims);
     return to_status(sa::launch_kv_append(a, (hipStream_t)stream));
 }
 
@@ -248,7 +257,9 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
                  (rope->style != SA_ROPE_HALF && rope->style != SA_ROPE_INTERLEAVED) || !k_new))
         return SA_ERR_INVALID_ARG;
     const bool valu = dims->variant == SA_VARIANT_VALU;
-    if (valu && (dims->num_q_heads / dims->num_kv_heads > 8 || k_new)) return SA_ERR_UNSUPPORTED;
+    if (valu && (dims->num_q_heads / dims->num_kv_heads > 8 || k_new || query_tokens(dims) > 1))
+        return SA_ERR_UNSUPPORTED;
+    if (rope && query_tokens(dims) > 1) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
     const Mode mode = choose_mode(dims, window, p);
@@ -308,7 +319,7 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     c.part_lse = a.part_lse;
     c.sinks = sinks;
     c.out = out;
-    c.B = a.B;
+    c.B = a.B * a.T;              // partial / out rows (b*T + t)*Hq + h
     c.Hq = a.Hq;
     c.num_splits = p.splits;
     return to_status(sa::launch_combine(c, s));
@@ -381,17 +392,20 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
                int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream) {
     if (!dims) return SA_ERR_INVALID_ARG;
-    if (dims->num_seqs < 0 || dims->num_q_heads < 1 || num_splits < 1) return SA_ERR_INVALID_ARG;
+    if (dims->num_seqs < 0 || dims->num_q_heads < 1 || num_splits < 1 ||
+        dims->num_query_tokens < 0)
+        return SA_ERR_INVALID_ARG;
     if (dims->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
     if (dims->num_seqs == 0) return SA_OK;
     if (!part_o || !part_lse || !out) return SA_ERR_INVALID_ARG;
-    if ((long long)dims->num_seqs * dims->num_q_heads >= INT_MAX) return SA_ERR_INVALID_ARG;
+    if ((long long)dims->num_seqs * query_tokens(dims) * dims->num_q_heads >= INT_MAX)
+        return SA_ERR_INVALID_ARG;
     sa::CombineArgs c{};
     c.part_o = part_o;
     c.part_lse = part_lse;
     c.sinks = sinks;
     c.out = out;
-    c.B = dims->num_seqs;
+    c.B = dims->num_seqs * query_tokens(dims);
     c.Hq = dims->num_q_heads;
     c.num_splits = num_splits;
     return to_status(sa::launch_combine(c, (hipStream_t)stream));

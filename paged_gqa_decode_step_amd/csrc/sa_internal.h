@@ -7,7 +7,8 @@
 namespace sa {
 
 constexpr int kHeadDim = 64;       // D handled by the kernels
-constexpr int kMaxGroup = 16;      // query heads per KV head (one MFMA column tile)
+constexpr int kMaxGroup = 16;      // query columns per KV head: (query tokens) x (heads
+                                   // per KV head) fill one 16-column MFMA tile
 constexpr int kStepTokens = 32;    // tokens per inner step of the partition kernels
 constexpr int kMaxTableSlice = 64; // block-table entries one partition may span
 
@@ -19,6 +20,7 @@ struct AppendArgs {
     const int32_t* block_table;
     const int32_t* seq_lens;
     int32_t B, Hkv, bs_log2, mbs, num_blocks, window;
+    int32_t T;                // new tokens per sequence (positions L-T .. L-1)
 };
 
 // What a partition kernel does with its result.
@@ -47,6 +49,8 @@ struct DecodeArgs {
                               // wavefront) of each unit with a step, for its combine
     int32_t num_waves;        // balanced kernel: wavefronts in the grid
     int32_t B, Hq, Hkv, G;
+    int32_t T;                // query tokens per sequence (1, or several: causal,
+                              // kernels built for it); q / out rows (b*T + t)*Hq + h
     int32_t bs_log2, mbs, num_blocks, window;
     int32_t num_splits;       // S
     int32_t part_tokens;      // P: slots per partition (multiple of 32 and of bs)
@@ -71,7 +75,8 @@ struct CombineArgs {
 };
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
-// rope: the kernels built with the rotary embedding of q and k_new
+// rope: the kernels built with the rotary embedding of q and k_new; a.T > 1:
+// the kernels built for several causal query tokens per sequence
 hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream);
 hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);

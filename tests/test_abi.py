@@ -66,6 +66,8 @@ def test_status_strings(lib):
     (dict(num_blocks=0), SA_ERR_INVALID_ARG),
     (dict(num_splits=-2), SA_ERR_INVALID_ARG),
     (dict(variant=9), SA_ERR_INVALID_ARG),
+    (dict(num_query_tokens=-1), SA_ERR_INVALID_ARG),
+    (dict(num_query_tokens=3), SA_ERR_UNSUPPORTED),               # 3 tokens x G 8 > 16
 ])
 def test_bad_dims_rejected_everywhere(lib, kw, status):
     d = good_dims(**kw)
@@ -183,3 +185,23 @@ def test_rope_entry_validates(lib):
     assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, ctypes.byref(good), FAKE,
                                                ctypes.byref(dv), FAKE, 1 << 30,
                                                None) == SA_ERR_UNSUPPORTED
+
+
+def test_query_tiles_need_a_full_layer_and_mfma(lib):
+    """Several query tokens: no ring window, no vector-ALU variant, no RoPE."""
+    d = good_dims(num_query_tokens=2)
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 0) >= 1
+    assert lib.sa_decode_num_splits(ctypes.byref(d), 16) == SA_ERR_UNSUPPORTED
+    assert lib.sa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, ctypes.byref(d),
+                            None) == SA_ERR_UNSUPPORTED
+    dv = good_dims(num_query_tokens=2, variant=3)
+    assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, ctypes.byref(dv),
+                                   FAKE, 1 << 30, None) == SA_ERR_UNSUPPORTED
+    r = sa.Rope(0x30000, 0x40000, 16, 0)
+    assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, ctypes.byref(r), FAKE,
+                                               ctypes.byref(d), FAKE, 1 << 30,
+                                               None) == SA_ERR_UNSUPPORTED
+    # the workspace grows with the tile (more partial rows)
+    d1, d2 = good_dims(num_splits=4), good_dims(num_splits=4, num_query_tokens=2)
+    assert lib.sa_decode_workspace_bytes(ctypes.byref(d2), 0) > \
+        lib.sa_decode_workspace_bytes(ctypes.byref(d1), 0)
