@@ -25,16 +25,21 @@ constexpr long kMinWaves = 128;
 // The fused mode (the last partition of a (b, g) merges the partials) is
 // never the default: measured on MI355X, the device-scope fence every
 // partition then needs costs more than the separate combine launch.
-// Balanced kernel: at most kStreamWaves wavefronts (8 per compute unit of an
-// MI355X; measured better than one full round of 12: fewer, longer streams
-// and fewer partials), at most kMaxSegsPerUnit per (sequence, KV head) so a
+// Balanced kernel: at most kStreamWaves wavefronts (4 per compute unit of an
+// MI355X, one per SIMD: measured faster than 6 or 8 per unit on every large
+// workload, since fewer, longer streams leave fewer partials and unit
+// switches while two steps in flight per wavefront still keep HBM busy),
+// rounded down to a multiple of kWaveQuantum above it (counts between, such
+// as 1280, 1664 or 1920, measured 5-8% slower), at most kMaxSegsPerUnit per
+// (sequence, KV head) so a
 // few long units do not turn into hundreds of partials each, and at least
 // kMinStreamSteps 32-slot steps of work each, for batches of up to
 // kMaxStreamSeqs sequences (its per-sequence table lives in LDS).
 #ifndef SA_STREAM_WAVES
-#define SA_STREAM_WAVES 2048
+#define SA_STREAM_WAVES 1024
 #endif
 constexpr long kStreamWaves = SA_STREAM_WAVES;
+constexpr long kWaveQuantum = 512;
 constexpr long kMaxSegsPerUnit = 128;
 constexpr long kMinStreamSteps = 8;
 constexpr int kMaxStreamSeqs = 2048;
@@ -128,7 +133,9 @@ long stream_waves(const sa_dims* d, int32_t window) {
     long nw = (t_upper + kMinStreamSteps - 1) / kMinStreamSteps;
     const long seg_cap = (long)d->num_seqs * d->num_kv_heads * kMaxSegsPerUnit;
     if (nw > seg_cap) nw = seg_cap;
-    return nw < 1 ? 1 : (nw > kStreamWaves ? kStreamWaves : nw);
+    if (nw > kStreamWaves) nw = kStreamWaves;
+    if (nw > kWaveQuantum) nw -= nw % kWaveQuantum;
+    return nw < 1 ? 1 : nw;
 }
 
 // Which kernel a call with these dims uses (assumes check_dims passed).
