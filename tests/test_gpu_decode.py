@@ -2,6 +2,7 @@
 mean-abs <= 2e-3), through the C ABI.  Sizes span several partitions and a
 ragged tail; the full-size workloads are checked in test_gpu_workloads.py."""
 
+import dataclasses
 import math
 
 import numpy as np
@@ -10,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tails
+from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tails, sub_layer
 
 pytestmark = pytest.mark.gpu
 
@@ -315,3 +316,50 @@ def test_short_sequences_under_a_large_capacity(lib, W):
                                    layer.seq_lens, layer.sinks, W, workspace=ws, variant=v)
         torch.cuda.synchronize()
         assert_parity(out_f64(out), ref, f"short under capacity W={W} v={v}")
+
+
+@pytest.mark.parametrize("W", [0, 128])
+def test_pools_past_4gib(lib, W):
+    """64-bit addressing: a layer's blocks moved to the top of pools of about
+    4.3 GB each, so every block the table names starts past byte 2^32 of its
+    pool.  Attention (every engine), the fused append and the standalone
+    append must give what the oracle gives for the same blocks in a small
+    pool."""
+    layer = synth.make_layer(batch=4, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
+                             lens=[3000, 17, 1000, 520], window=W, seed=9100 + W,
+                             device="cuda")
+    nb = layer.k_cache.shape[0]
+    block_bytes = layer.k_cache[0].numel() * layer.k_cache.element_size()
+    off = (1 << 32) // block_bytes + 1000
+    assert off * block_bytes > (1 << 32)
+    big_k = torch.empty((off + nb,) + tuple(layer.k_cache.shape[1:]), dtype=layer.k_cache.dtype,
+                        device="cuda")
+    big_v = torch.empty((off + nb,) + tuple(layer.v_cache.shape[1:]), dtype=layer.v_cache.dtype,
+                        device="cuda")
+    big_k[off:] = layer.k_cache
+    big_v[off:] = layer.v_cache
+    big = dataclasses.replace(layer, k_cache=big_k, v_cache=big_v,
+                              block_table=layer.block_table + off,
+                              poison_block=layer.poison_block + off)
+    ref = oracle_attention(layer)
+    for v in VARIANTS:
+        assert_parity(out_f64(attend(lib, big, variant=v)), ref, f"W={W} variant={v}")
+    # the appends write past 4 GiB too: compare the moved blocks bit for bit
+    s = sub_layer(layer, range(layer.batch))
+    k_ref, v_ref = oracle.kv_append(s["k"], s["v"], s["k_new"], s["v_new"], s["bt"], s["lens"], W)
+    ref_after = oracle.decode_attention(s["q"], k_ref, v_ref, s["bt"], s["lens"], s["sinks"], W)
+    for v in (0, 1, 2, 4):
+        kc, vc = big_k.clone(), big_v.clone()
+        run = dataclasses.replace(big, k_cache=kc, v_cache=vc)
+        out = lib.decode_attention_append(run.q, run.k_new, run.v_new, kc, vc, run.block_table,
+                                          run.seq_lens, run.sinks, W, variant=v)
+        torch.cuda.synchronize()
+        after = sub_layer(run, range(layer.batch))
+        assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref), \
+            f"W={W} variant={v}: pools after the fused append"
+        assert_parity(out_f64(out), ref_after, f"W={W} fused variant={v}")
+        del kc, vc, run
+    lib.kv_append(big.k_new, big.v_new, big_k, big_v, big.block_table, big.seq_lens, W)
+    torch.cuda.synchronize()
+    after = sub_layer(big, range(layer.batch))
+    assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref)
