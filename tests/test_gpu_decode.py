@@ -363,3 +363,26 @@ def test_pools_past_4gib(lib, W):
     torch.cuda.synchronize()
     after = sub_layer(big, range(layer.batch))
     assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref)
+
+
+@pytest.mark.parametrize("B", [2048, 2049])
+def test_batch_at_the_balanced_limit(lib, B):
+    """2048 sequences is the most the balanced kernel takes (its per-sequence
+    lengths and step prefix sit in LDS); one more and every call goes to the
+    static split.  Attention and the fused append, every sequence checked."""
+    lens = np.random.default_rng(B).integers(1, 300, size=B)
+    layer = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=lens, seed=9200 + B, device="cuda")
+    ref = oracle_attention(layer)
+    for v in (0, 4):
+        assert_parity(out_f64(attend(lib, layer, variant=v)), ref, f"B={B} variant={v}")
+    s = sub_layer(layer, range(B))
+    k_ref, v_ref = oracle.kv_append(s["k"], s["v"], s["k_new"], s["v_new"], s["bt"], s["lens"], 0)
+    ref_after = oracle.decode_attention(s["q"], k_ref, v_ref, s["bt"], s["lens"], s["sinks"], 0)
+    out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, layer.k_cache,
+                                      layer.v_cache, layer.block_table, layer.seq_lens,
+                                      layer.sinks, 0)
+    torch.cuda.synchronize()
+    after = sub_layer(layer, range(B))
+    assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref)
+    assert_parity(out_f64(out), ref_after, f"B={B} fused")
