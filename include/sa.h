@@ -68,7 +68,9 @@ typedef struct sa_dims {
     int32_t num_kv_heads;        /* Hkv                                         */
     int32_t head_dim;            /* D: 64                                       */
     int32_t block_size;          /* bs: 8, 16, 32 or 64 tokens per block        */
-    int32_t max_blocks_per_seq;  /* row stride of block_table                   */
+    int32_t max_blocks_per_seq;  /* row stride of block_table; the capacity
+                                    max_blocks_per_seq * bs is at most 2^30
+                                    tokens (SA_ERR_UNSUPPORTED otherwise)      */
     int32_t num_blocks;          /* blocks in each pool                         */
     int32_t num_splits;          /* 0: the library's fixed split table;
                                     > 0: use at most this many split-K
@@ -88,7 +90,8 @@ typedef struct sa_dims {
 enum {
     SA_OK = 0,
     SA_ERR_INVALID_ARG = -1,    /* NULL pointer, negative or inconsistent size  */
-    SA_ERR_UNSUPPORTED = -2,    /* D != 64, Hq % Hkv != 0, Hq/Hkv > 16, bs, ... */
+    SA_ERR_UNSUPPORTED = -2,    /* D != 64, Hq % Hkv != 0, Hq/Hkv > 16, bs,
+                                   capacity > 2^30 tokens, ...                  */
     SA_ERR_WORKSPACE = -3,      /* workspace missing or too small               */
     SA_ERR_HIP = -4             /* the HIP runtime refused a launch             */
 };

@@ -93,8 +93,9 @@ void decode_stream_kernel(const DecodeArgs a) {
         for (int bz = i; bz < a.B; bz += NW) finish_empty(a, bz, i, lane);
         return;
     }
-    // step counts stay below 2^31 (sequences x KV heads x 2^26 slots / 32),
-    // so the walk runs on 32-bit wave-uniform values
+    // the host launches this kernel only when sequences x KV heads x the
+    // table's capacity in steps stays below 2^31, so the walk runs on 32-bit
+    // wave-uniform values
     if (i == 0)                   // sequences before the first with a step
         for (int bz = 0; bz < a.B && s_end[bz] == 0; ++bz) finish_empty(a, bz, 0, lane);
     // The launch sizes NW from the table's capacity; with fewer steps than

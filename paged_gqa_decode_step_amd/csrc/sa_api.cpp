@@ -73,6 +73,9 @@ int check_dims(const sa_dims* d, int32_t window) {
         return SA_ERR_INVALID_ARG;
     if ((long long)d->num_blocks * d->num_kv_heads * d->block_size * kHeadDim > (1LL << 40))
         return SA_ERR_INVALID_ARG;
+    // a sequence's capacity in tokens, and slot arithmetic past it by one
+    // partition, stay in the device's 32-bit ints
+    if ((long long)d->max_blocks_per_seq * d->block_size > (1LL << 30)) return SA_ERR_UNSUPPORTED;
     return SA_OK;
 }
 
@@ -123,13 +126,18 @@ struct WorkspaceLayout {
 
 enum class Mode { kStatic, kFused, kBalanced };
 
-// Wavefronts of the balanced kernel for these dims (an upper bound on the
-// work is all the host knows: the lengths live on the device).
-long stream_waves(const sa_dims* d, int32_t window) {
+// Upper bound on the balanced kernel's steps for these dims: every unit at
+// the table's capacity (the lengths live on the device).
+long stream_steps_upper(const sa_dims* d, int32_t window) {
     const long cap = (long)d->max_blocks_per_seq * d->block_size;
     const long max_n = window > 0 ? (window < cap ? window : cap) : cap;
-    const long t_upper = (long)d->num_seqs * d->num_kv_heads *
-                         ((max_n + sa::kStepTokens - 1) / sa::kStepTokens);
+    return (long)d->num_seqs * d->num_kv_heads * ((max_n + sa::kStepTokens - 1) / sa::kStepTokens);
+}
+
+// Wavefronts of the balanced kernel for these dims (an upper bound on the
+// work is all the host knows).
+long stream_waves(const sa_dims* d, int32_t window) {
+    const long t_upper = stream_steps_upper(d, window);
     long nw = (t_upper + kMinStreamSteps - 1) / kMinStreamSteps;
     const long seg_cap = (long)d->num_seqs * d->num_kv_heads * kMaxSegsPerUnit;
     if (nw > seg_cap) nw = seg_cap;
@@ -140,7 +148,10 @@ long stream_waves(const sa_dims* d, int32_t window) {
 
 // Which kernel a call with these dims uses (assumes check_dims passed).
 Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
-    const bool fits_stream = d->num_seqs <= kMaxStreamSeqs;
+    // the balanced kernel keeps its per-sequence table in LDS and walks steps
+    // in 32-bit arithmetic
+    const bool fits_stream =
+        d->num_seqs <= kMaxStreamSeqs && stream_steps_upper(d, window) <= INT_MAX;
     switch (d->variant) {
         case SA_VARIANT_MFMA_BALANCED:
             return fits_stream ? Mode::kBalanced : Mode::kStatic;

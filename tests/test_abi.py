@@ -68,6 +68,7 @@ def test_status_strings(lib):
     (dict(variant=9), SA_ERR_INVALID_ARG),
     (dict(num_query_tokens=-1), SA_ERR_INVALID_ARG),
     (dict(num_query_tokens=3), SA_ERR_UNSUPPORTED),               # 3 tokens x G 8 > 16
+    (dict(max_blocks_per_seq=1 << 27), SA_ERR_UNSUPPORTED),       # capacity 2^31 tokens
 ])
 def test_bad_dims_rejected_everywhere(lib, kw, status):
     d = good_dims(**kw)
@@ -205,3 +206,14 @@ def test_query_tiles_need_a_full_layer_and_mfma(lib):
     d1, d2 = good_dims(num_splits=4), good_dims(num_splits=4, num_query_tokens=2)
     assert lib.sa_decode_workspace_bytes(ctypes.byref(d2), 0) > \
         lib.sa_decode_workspace_bytes(ctypes.byref(d1), 0)
+
+
+def test_balanced_kernel_only_below_2_31_steps(lib):
+    """The balanced kernel walks its steps in 32-bit arithmetic: when the
+    table's capacity could give more than 2^31 - 1 steps the call takes the
+    static split, whose workspace holds every partition's partials (here far
+    larger than the balanced kernel's few MB)."""
+    small = good_dims(num_seqs=2048, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=1 << 16)
+    big = good_dims(num_seqs=2048, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=1 << 19)
+    assert lib.sa_decode_workspace_bytes(ctypes.byref(small), 0) < (64 << 20)
+    assert lib.sa_decode_workspace_bytes(ctypes.byref(big), 0) > (1 << 36)
