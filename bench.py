@@ -99,7 +99,8 @@ def make_workload(name, device, seed_offset=0):
     import synth
     if name == "batch64_ragged":
         return ragged_layers(device, seed_offset)
-    if name in ("tiny", "batch64_8k", "gptoss_layer_8k", "long_131k_b1", "long_131k_b8"):
+    if name in ("tiny", "batch64_8k", "gptoss_layer_8k", "long_131k_b1", "long_131k_b8",
+                "long_131k_b8_tp_share"):
         c = dict(synth.CONFIGS[name])
         c["seed"] += seed_offset
         return [synth.make_layer(device=device, **c)]
@@ -633,7 +634,8 @@ def main():
         for nm, kw in (("batch64_8k", dict(oracle_seqs=[0, 21, 42, 63],
                                            label="batch64_8k (headline)")),
                        ("tiny", {}), ("gptoss_layer_8k", {}), ("long_131k_b1", {}),
-                       ("long_131k_b8", dict(oracle_seqs=[3]))):
+                       ("long_131k_b8", dict(oracle_seqs=[3])),
+                       ("long_131k_b8_tp_share", dict(oracle_seqs=[3]))):
             e, h = attention_config(sa, torch, timer, dev, nm, steps=args.steps,
                                     warmup=args.warmup, variant=args.variant, with_oracle=oc,
                                     **kw)

@@ -196,6 +196,10 @@ CONFIGS = {
                          lens=[131072], window=0, seed=1004),
     "long_131k_b8": dict(batch=8, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
                          lens=[131072] * 8, window=0, seed=1005),
+    # one GPU's share of long_131k_b8 with the KV heads split over 8 GPUs
+    # (tensor parallelism): 8 query heads / 1 KV head per GPU
+    "long_131k_b8_tp_share": dict(batch=8, q_heads=8, kv_heads=1, head_dim=64, block_size=16,
+                                  lens=[131072] * 8, window=0, seed=1008),
     # decode loop: 24 layers alternating ring-128 / full, batch 64, initial
     # ragged lengths 1024..32768, 50 steps of one appended token per sequence
     "decode_loop": dict(batch=64, q_heads=64, kv_heads=8, head_dim=64, block_size=16,

@@ -386,3 +386,33 @@ def test_batch_at_the_balanced_limit(lib, B):
     after = sub_layer(layer, range(B))
     assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref)
     assert_parity(out_f64(out), ref_after, f"B={B} fused")
+
+
+def test_context_parallel_shards_merge(lib):
+    """Context parallelism as it would run over several GPUs, emulated on one:
+    each sequence's blocks are cut into R contiguous shards; every shard's
+    partials come from sa_decode_partials over its own slice of the block
+    table (its slots counted from 0: full attention does not depend on where
+    a slot sits), and one sa_combine over all shards' partials, which is what
+    the exchange would deliver, gives the whole attention.  Shape: one GPU's
+    tensor-parallel share of the long-context layer (8 query heads, 1 KV
+    head); a short sequence leaves whole shards empty."""
+    R, bs = 4, 16
+    layer = synth.make_layer(batch=3, q_heads=8, kv_heads=1, head_dim=64, block_size=bs,
+                             lens=[20000, 7777, 33], seed=9300, device="cuda")
+    ref = oracle_attention(layer)
+    mbs = layer.block_table.shape[1]
+    per = math.ceil(mbs / R)
+    pos, pls = [], []
+    for r in range(R):
+        lo, hi = r * per, min(mbs, (r + 1) * per)
+        table = layer.block_table[:, lo:hi].contiguous()
+        lens = (layer.seq_lens - lo * bs).clamp(min=0, max=(hi - lo) * bs).to(torch.int32)
+        po, pl = lib.decode_partials(layer.q, layer.k_cache, layer.v_cache, table, lens, 0)
+        pos.append(po)
+        pls.append(pl)
+    torch.cuda.synchronize()
+    out = lib.combine(torch.cat(pos, dim=2).contiguous(), torch.cat(pls, dim=2).contiguous(),
+                      layer.sinks)
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), ref, f"{R} context shards merged")

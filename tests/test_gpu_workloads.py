@@ -57,7 +57,8 @@ def test_batch64_uniform_8k_sampled(lib):
     assert np.isfinite(got).all()
 
 
-@pytest.mark.parametrize("name,seqs", [("long_131k_b1", [0]), ("long_131k_b8", [0, 5])])
+@pytest.mark.parametrize("name,seqs", [("long_131k_b1", [0]), ("long_131k_b8", [0, 5]),
+                                       ("long_131k_b8_tp_share", [1, 6])])
 def test_long_context(lib, name, seqs):
     layer = synth.make_layer(device="cuda", **synth.CONFIGS[name])
     S = lib.num_splits(layer.q, layer.k_cache, layer.v_cache, layer.block_table, 0)
