@@ -135,8 +135,9 @@ void decode_stream_kernel(const DecodeArgs a) {
         const Unit u = make_unit(a, b, g, lane, MULTI ? -1 : new_token_slot(a, L, n), pos, L);
         State st;
         st.reset();
-        attend<BSL, ROPE, MULTI>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1,
-                                 st);
+        // one wavefront per SIMD: three steps in the register pipeline
+        attend<BSL, ROPE, MULTI, 3>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1,
+                                    st);
         const float l_tot = st.total();
         if (lane == 0) {
             int* seg = a.unit_seg + 2 * (b * a.Hkv + g);

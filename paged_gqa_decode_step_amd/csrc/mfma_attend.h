@@ -303,7 +303,7 @@ __device__ __forceinline__ int table_slice(const Unit& u, int blk0, int lane) {
 // the run spanning at most kMaxTableSlice blocks, whose table entries tbl
 // holds), folding into st.  kword / vval: this lane's word (lane & 31) of the
 // new token's K row and its element `lane` of the V row.
-template <int BSL, bool ROPE, bool MULTI>
+template <int BSL, bool ROPE, bool MULTI, int DEPTH>
 __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl,
                                            unsigned kword, uint16_t vval, float2 kcos,
                                            float2 ksin, int rope_style, u32x4_t qop0,
@@ -466,6 +466,66 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         }
     }
 
+    if constexpr (DEPTH == 3) {
+        // Three register sets: the loads of steps s+1 and s+2 are in flight
+        // while step s computes (for a kernel that runs one wavefront per
+        // SIMD, where the extra 32 registers cost no occupancy).  Runs of one
+        // or two steps, and the one to four steps after the last whole
+        // triple, are peeled so that no load reaches past the run or sits
+        // under a branch that joins before its use.
+        StepRegs A, B, C;
+        if (nsteps == 1) {
+            load_step(0, A);
+            if (has_new && !new_first) store_new();
+            compute_step(0, A);
+        } else if (nsteps == 2) {
+            load_step(0, A);
+            if (has_new && !new_first) store_new();
+            load_step(1, B);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(0, A);
+            compute_step(1, B);
+        } else {
+            load_step(0, A);
+            if (has_new && !new_first) store_new();
+            load_step(1, B);
+            int s = 0;
+            // steps s and s+1 are in flight at the top of each triple
+            for (; s + 5 <= nsteps; s += 3) {
+                load_step(s + 2, C);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s, A);
+                load_step(s + 3, A);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s + 1, B);
+                load_step(s + 4, B);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s + 2, C);
+            }
+            const int r = nsteps - s;            // 2, 3 or 4 steps left
+            if (r == 2) {
+                compute_step(s, A);
+                compute_step(s + 1, B);
+            } else if (r == 3) {
+                load_step(s + 2, C);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s, A);
+                compute_step(s + 1, B);
+                compute_step(s + 2, C);
+            } else {
+                load_step(s + 2, C);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s, A);
+                load_step(s + 3, A);
+                __builtin_amdgcn_sched_barrier(0);
+                compute_step(s + 1, B);
+                compute_step(s + 2, C);
+                compute_step(s + 3, A);
+            }
+        }
+        return;
+    }
+
     // Two register sets in ping-pong: the loads of step s+1 are in flight
     // while step s computes.  The loop covers whole pairs that still have a
     // next step to prefetch; the last one or two steps are peeled, so no load
@@ -498,7 +558,8 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
 // blocks (t0 a multiple of 32).  The first run's table slice and the new
 // token's words are read here, with no branch, so they travel with the
 // caller's query loads.
-template <int BSL, bool ROPE, bool MULTI = false>
+// DEPTH: register sets of the step pipeline (2, or 3 for one wavefront per SIMD).
+template <int BSL, bool ROPE, bool MULTI = false, int DEPTH = 2>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t0, int t1,
                                        u32x4_t qop0, u32x4_t qop1, State& st) {
     constexpr int run = kMaxTableSlice << BSL;
@@ -521,8 +582,8 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
     }
     for (int r0 = t0;;) {
         const int r1 = min(t1, r0 + run);
-        attend_run<BSL, ROPE, MULTI>(u, r0, r1, tbl, kword, vval, kcos, ksin, a.rope_style, qop0,
-                                     qop1, st);
+        attend_run<BSL, ROPE, MULTI, DEPTH>(u, r0, r1, tbl, kword, vval, kcos, ksin,
+                                            a.rope_style, qop0, qop1, st);
         if (r1 >= t1) break;
         r0 = r1;
         tbl = table_slice(u, r0 >> BSL, lane);
