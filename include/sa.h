@@ -23,6 +23,9 @@
  *    synchronisation.
  *  - Errors are negative SA_ERR_* codes returned before anything is
  *    launched; no call aborts or throws.
+ *  - q, out, k_new, v_new, k_cache, v_cache, part_o, the rotary tables and
+ *    the workspace are read or written 16 bytes at a time and must be
+ *    16-byte aligned (SA_ERR_INVALID_ARG otherwise).
  *  - Shapes: B sequences, Hq query heads, Hkv KV heads (Hq % Hkv == 0,
  *    Hq/Hkv <= 16), head_dim D == 64, block_size bs in {8, 16, 32, 64}.
  *  - GQA: query head h reads KV head h / (Hq/Hkv) (contiguous groups).

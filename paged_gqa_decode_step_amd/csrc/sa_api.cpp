@@ -3,6 +3,7 @@
 // Nothing here allocates, frees or synchronises; every call checks its
 // arguments completely before it enqueues any kernel on the caller's stream.
 #include <limits.h>
+#include <stdint.h>
 #include <math.h>
 
 #include "../../include/sa.h"
@@ -43,6 +44,12 @@ constexpr long kWaveQuantum = 512;
 constexpr long kMaxSegsPerUnit = 128;
 constexpr long kMinStreamSteps = 8;
 constexpr int kMaxStreamSeqs = 2048;
+
+// 16-byte vector accesses need 16-byte aligned bases (null passes: the
+// null checks are separate)
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+template <typename... P>
+bool all_aligned16(const P*... p) { return (aligned16(p) && ...); }
 
 int log2_exact(int x) {
     int l = 0;
@@ -226,6 +233,7 @@ int sa_kv_append(const sa_bf16* k_new, const sa_bf16* v_new, sa_bf16* k_cache,
     if (dims->num_seqs == 0) return SA_OK;
     if (!k_new || !v_new || !k_cache || !v_cache || !block_table || !seq_lens)
         return SA_ERR_INVALID_ARG;
+    if (!all_aligned16(k_new, v_new, k_cache, v_cache)) return SA_ERR_INVALID_ARG;
     if ((long long)dims->num_seqs * dims->num_kv_heads >= INT_MAX) return SA_ERR_INVALID_ARG;
     sa::AppendArgs a{};
     a.k_new = k_new;
@@ -271,8 +279,11 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     if (dims->num_seqs == 0) return SA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !out)
         return SA_ERR_INVALID_ARG;
+    if (!all_aligned16(q, k_cache, v_cache, out, k_new, v_new, workspace))
+        return SA_ERR_INVALID_ARG;
     if (rope && (!rope->cos_table || !rope->sin_table || rope->max_positions < 1 ||
-                 (rope->style != SA_ROPE_HALF && rope->style != SA_ROPE_INTERLEAVED) || !k_new))
+                 (rope->style != SA_ROPE_HALF && rope->style != SA_ROPE_INTERLEAVED) || !k_new ||
+                 !all_aligned16(rope->cos_table, rope->sin_table)))
         return SA_ERR_INVALID_ARG;
     const bool valu = dims->variant == SA_VARIANT_VALU;
     if (valu && (dims->num_q_heads / dims->num_kv_heads > 8 || k_new || query_tokens(dims) > 1))
@@ -392,6 +403,7 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
     if (dims->num_seqs == 0) return SA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !part_o || !part_lse)
         return SA_ERR_INVALID_ARG;
+    if (!all_aligned16(q, k_cache, v_cache, part_o)) return SA_ERR_INVALID_ARG;
     if (dims->variant == SA_VARIANT_VALU) return SA_ERR_UNSUPPORTED;
     const Plan p = plan(dims, window);
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;

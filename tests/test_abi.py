@@ -217,3 +217,24 @@ def test_balanced_kernel_only_below_2_31_steps(lib):
     big = good_dims(num_seqs=2048, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=1 << 19)
     assert lib.sa_decode_workspace_bytes(ctypes.byref(small), 0) < (64 << 20)
     assert lib.sa_decode_workspace_bytes(ctypes.byref(big), 0) > (1 << 36)
+
+
+def test_misaligned_pointers_rejected(lib):
+    """Pointers read or written 16 bytes at a time must be 16-byte aligned;
+    a misaligned one is refused before anything is launched."""
+    d = ctypes.byref(good_dims())
+    odd = ctypes.c_void_p(0x10008)
+    ok = FAKE
+    assert lib.sa_kv_append(odd, ok, ok, ok, ok, ok, 0, d, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_kv_append(ok, ok, ok, odd, ok, ok, 0, d, None) == SA_ERR_INVALID_ARG
+    for i in (0, 1, 2, 7):            # q, k_cache, v_cache, out
+        args = [ok, ok, ok, ok, ok, ok, 0, ok, d, ok, 1 << 30, None]
+        args[i] = odd
+        assert lib.sa_decode_attention(*args) == SA_ERR_INVALID_ARG, i
+    assert lib.sa_decode_attention(ok, ok, ok, ok, ok, ok, 0, ok, d, odd, 1 << 30,
+                                   None) == SA_ERR_INVALID_ARG        # workspace
+    for i in (1, 2):                  # k_new, v_new
+        args = [ok, ok, ok, ok, ok, ok, ok, ok, 0, ok, d, ok, 1 << 30, None]
+        args[i] = odd
+        assert lib.sa_decode_attention_append(*args) == SA_ERR_INVALID_ARG, i
+    assert lib.sa_decode_partials(ok, ok, ok, ok, ok, 0, odd, ok, d, None) == SA_ERR_INVALID_ARG
