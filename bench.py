@@ -47,7 +47,7 @@ METRIC = "decode-attn µs/call + achieved HBM GB/s (% of peak), batch 64, 8k ctx
 # sources of the dominant call's kernels; the committed counter summary is
 # valid only for the exact sources it was taken on
 KERNEL_SRCS = [os.path.join(_ROOT, "paged_gqa_decode_step_amd", "csrc", f)
-               for f in ("decode_stream.hip", "mfma_attend.h", "sa_api.cpp")]
+               for f in ("decode_stream.hip", "mfma_attend.h", "sa_internal.h", "plan.h")]
 TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "decode_attention_batch64_ragged_traffic.json")
 
 

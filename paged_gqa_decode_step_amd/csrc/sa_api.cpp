@@ -1,4 +1,5 @@
-// C-ABI layer of libsa: argument checks, the fixed split table, launches.
+// C-ABI layer of libsa: argument checks and launches (the launch planning,
+// split table and workspace layout, is plan.h).
 //
 // Nothing here allocates, frees or synchronises; every call checks its
 // arguments completely before it enqueues any kernel on the caller's stream.
@@ -7,43 +8,12 @@
 #include <math.h>
 
 #include "../../include/sa.h"
+#include "plan.h"
 #include "sa_internal.h"
 
 namespace {
 
 using sa::kHeadDim;
-
-// Fixed split table (no autotuning, so the result of a call never depends on
-// timing).  A partition is 32 * 2^k slots, at most kMaxTableSlice blocks and
-// at most kMaxPartTokens slots, and never longer than the context capacity
-// (a 128-slot ring is one partition).  It halves, down to kMinPartTokens,
-// while a call would have fewer than kMinWaves partition wavefronts.  Chosen
-// from measured sweeps on MI355X: long partitions keep the partial traffic
-// and the combine small; batch-1 calls trade some of that for parallelism.
-constexpr int kMaxPartTokens = 1024;
-constexpr int kMinPartTokens = 256;
-constexpr long kMinWaves = 128;
-// The fused mode (the last partition of a (b, g) merges the partials) is
-// never the default: measured on MI355X, the device-scope fence every
-// partition then needs costs more than the separate combine launch.
-// Balanced kernel: at most kStreamWaves wavefronts (4 per compute unit of an
-// MI355X, one per SIMD: measured faster than 6 or 8 per unit on every large
-// workload, since fewer, longer streams leave fewer partials and unit
-// switches while two steps in flight per wavefront still keep HBM busy),
-// rounded down to a multiple of kWaveQuantum above it (counts between, such
-// as 1280, 1664 or 1920, measured 5-8% slower), at most kMaxSegsPerUnit per
-// (sequence, KV head) so a
-// few long units do not turn into hundreds of partials each, and at least
-// kMinStreamSteps 32-slot steps of work each, for batches of up to
-// kMaxStreamSeqs sequences (its per-sequence table lives in LDS).
-#ifndef SA_STREAM_WAVES
-#define SA_STREAM_WAVES 1024
-#endif
-constexpr long kStreamWaves = SA_STREAM_WAVES;
-constexpr long kWaveQuantum = 512;
-constexpr long kMaxSegsPerUnit = 128;
-constexpr long kMinStreamSteps = 8;
-constexpr int kMaxStreamSeqs = 2048;
 
 // 16-byte vector accesses need 16-byte aligned bases (null passes: the
 // null checks are separate)
@@ -56,9 +26,6 @@ int log2_exact(int x) {
     while ((1 << l) < x) ++l;
     return (1 << l) == x ? l : -1;
 }
-
-// T: new tokens (query tokens) per sequence
-int query_tokens(const sa_dims* d) { return d->num_query_tokens > 0 ? d->num_query_tokens : 1; }
 
 int check_dims(const sa_dims* d, int32_t window) {
     if (!d) return SA_ERR_INVALID_ARG;
@@ -84,117 +51,6 @@ int check_dims(const sa_dims* d, int32_t window) {
     // partition, stay in the device's 32-bit ints
     if ((long long)d->max_blocks_per_seq * d->block_size > (1LL << 30)) return SA_ERR_UNSUPPORTED;
     return SA_OK;
-}
-
-struct Plan {
-    int32_t splits;
-    int32_t part_tokens;
-};
-
-// Assumes check_dims passed.
-Plan plan(const sa_dims* d, int32_t window) {
-    const int bs = d->block_size;
-    const long cap = (long)d->max_blocks_per_seq * bs;
-    const long max_n = window > 0 ? (window < cap ? window : cap) : cap;
-    const int gran = bs > sa::kStepTokens ? bs : sa::kStepTokens;
-    int pmax = sa::kMaxTableSlice * bs;
-    if (pmax > kMaxPartTokens && kMaxPartTokens >= gran) pmax = kMaxPartTokens;
-    int P;
-    if (d->num_splits > 0) {
-        long want = (max_n + d->num_splits - 1) / d->num_splits;
-        want = (want + gran - 1) / gran * gran;
-        P = (int)(want < gran ? gran : (want > pmax ? pmax : want));
-    } else {
-        const long units = (long)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
-        P = pmax;
-        while (P / 2 >= gran && P / 2 >= max_n) P /= 2;          // one partition covers it
-        while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
-               units * ((max_n + P - 1) / P) < kMinWaves)
-            P /= 2;
-    }
-    Plan p;
-    p.part_tokens = P;
-    p.splits = (int32_t)((max_n + P - 1) / P);
-    return p;
-}
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-// Workspace layout.  The completion counters of the fused combine sit at a
-// fixed place, offset 0, in a region nothing else ever writes: every call
-// returns the counters it used to zero, so a workspace zeroed once stays
-// valid for any later call, whatever its dims or split count.
-constexpr int kCounterSlots = 1 << 16;   // (sequence, KV head) pairs a fused call may have
-constexpr size_t kCounterBytes = (size_t)kCounterSlots * sizeof(int32_t);
-
-struct WorkspaceLayout {
-    size_t part_o, part_lse, counters, unit_seg, total;
-};
-
-enum class Mode { kStatic, kFused, kBalanced };
-
-// Upper bound on the balanced kernel's steps for these dims: every unit at
-// the table's capacity (the lengths live on the device).
-long stream_steps_upper(const sa_dims* d, int32_t window) {
-    const long cap = (long)d->max_blocks_per_seq * d->block_size;
-    const long max_n = window > 0 ? (window < cap ? window : cap) : cap;
-    return (long)d->num_seqs * d->num_kv_heads * ((max_n + sa::kStepTokens - 1) / sa::kStepTokens);
-}
-
-// Wavefronts of the balanced kernel for these dims (an upper bound on the
-// work is all the host knows).
-long stream_waves(const sa_dims* d, int32_t window) {
-    const long t_upper = stream_steps_upper(d, window);
-    long nw = (t_upper + kMinStreamSteps - 1) / kMinStreamSteps;
-    const long seg_cap = (long)d->num_seqs * d->num_kv_heads * kMaxSegsPerUnit;
-    if (nw > seg_cap) nw = seg_cap;
-    if (nw > kStreamWaves) nw = kStreamWaves;
-    if (nw > kWaveQuantum) nw -= nw % kWaveQuantum;
-    return nw < 1 ? 1 : nw;
-}
-
-// Which kernel a call with these dims uses (assumes check_dims passed).
-Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
-    // the balanced kernel keeps its per-sequence table in LDS and walks steps
-    // in 32-bit arithmetic
-    const bool fits_stream =
-        d->num_seqs <= kMaxStreamSeqs && stream_steps_upper(d, window) <= INT_MAX;
-    switch (d->variant) {
-        case SA_VARIANT_MFMA_BALANCED:
-            return fits_stream ? Mode::kBalanced : Mode::kStatic;
-        case SA_VARIANT_MFMA_FUSED:
-            return (long long)d->num_seqs * d->num_kv_heads <= kCounterSlots ? Mode::kFused
-                                                                             : Mode::kStatic;
-        case SA_VARIANT_MFMA_TWO_PASS:
-        case SA_VARIANT_VALU:
-            return Mode::kStatic;
-        default:
-            // one static partition needs no merge at all; beyond that the
-            // balanced kernel keeps every compute unit equally busy
-            if (d->num_splits > 0 || p.splits == 1 || !fits_stream) return Mode::kStatic;
-            return Mode::kBalanced;
-    }
-}
-
-WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p, Mode m) {
-    WorkspaceLayout w{};
-    size_t rows, lse;        // partial rows of D floats, and lse entries
-    if (m == Mode::kBalanced) {
-        const size_t slots = (size_t)stream_waves(d, window) * 2 * query_tokens(d) *
-                             (d->num_q_heads / d->num_kv_heads);
-        rows = slots;
-        lse = slots;
-    } else {
-        if (p.splits <= 1) return w;
-        rows = (size_t)d->num_seqs * query_tokens(d) * d->num_q_heads * p.splits;
-        lse = rows;
-    }
-    w.counters = 0;
-    w.part_o = kCounterBytes;
-    w.part_lse = w.part_o + align256(rows * kHeadDim * sizeof(float));
-    w.unit_seg = w.part_lse + align256(lse * sizeof(float));
-    w.total = w.unit_seg + align256((size_t)d->num_seqs * d->num_kv_heads * 2 * sizeof(int32_t));
-    return w;
 }
 
 bool grid_fits(const sa_dims* d, int32_t splits) {
