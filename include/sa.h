@@ -33,7 +33,9 @@
  *      q, out          bf16 [B][Hq][D]
  *      k_new, v_new    bf16 [B][Hkv][D]
  *      k_cache         bf16 [num_blocks][Hkv][bs][D]
- *      v_cache         bf16 [num_blocks][Hkv][D][bs]   (V transposed in a block)
+ *      v_cache         bf16 [num_blocks][Hkv][bs/8][D][8]
+ *                      (V transposed inside a block in chunks of 8 slots:
+ *                       slot s, dim d at [s/8][d][s%8])
  *      block_table     int32 [B][max_blocks_per_seq]
  *      seq_lens        int32 [B]
  *      sinks           fp32 [Hq] (may be NULL: no sink)

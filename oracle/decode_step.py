@@ -27,7 +27,9 @@ concepts; the readings taken where the pages are silent are:
   full-attention layer over the paged cache;
 * cache layout (the library's documented layout, restated here on its own):
   K pool ``[num_blocks][Hkv][block_size][D]`` and V pool
-  ``[num_blocks][Hkv][D][block_size]`` (V transposed inside a block);
+  ``[num_blocks][Hkv][block_size/c][D][c]`` (V transposed inside a block in
+  chunks of c slots: slot s, dimension d at ``[s // c][d][s % c]``; the
+  library's c is 8, the pool's last axis gives it);
   ``block_table[b][j]`` is the physical block holding slots
   ``[j*block_size, (j+1)*block_size)`` of sequence b.
 
@@ -103,7 +105,8 @@ def _gather(k_cache, v_cache, block_table, b, g, positions, window):
     p = np.asarray(positions, dtype=np.int64)
     blks, offs = locate(block_table, b, storage_slot(p, window), k_cache.shape[2])
     K = bf16_bits_to_f64(k_cache[blks, g, offs, :])          # [n, D]
-    V = bf16_bits_to_f64(v_cache[blks, g, :, offs])          # [n, D]
+    c = v_cache.shape[-1]                                    # slots per V chunk
+    V = bf16_bits_to_f64(v_cache[blks, g, offs // c, :, offs % c])   # [n, D]
     return K, V
 
 
@@ -236,6 +239,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
     v = np.array(v_cache, copy=True)
     bs = k.shape[2]
     Hkv = k.shape[1]
+    c = v.shape[-1]                                          # slots per V chunk
     for b in range(len(seq_lens)):
         L = int(seq_lens[b])
         if L <= 0:
@@ -244,5 +248,5 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
         blk, off = int(blk), int(off)
         for g in range(Hkv):
             k[blk, g, off, :] = k_new[b, g, :]
-            v[blk, g, :, off] = v_new[b, g, :]
+            v[blk, g, off // c, :, off % c] = v_new[b, g, :]
     return k, v

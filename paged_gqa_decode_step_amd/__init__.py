@@ -10,8 +10,9 @@ call raises.
 
 Layouts (see include/sa.h): q/out ``[B][Hq][D]`` bf16; k_new/v_new
 ``[B][Hkv][D]`` bf16; k_cache ``[NB][Hkv][bs][D]`` bf16; v_cache
-``[NB][Hkv][D][bs]`` bf16; block_table ``[B][MBS]`` int32; seq_lens ``[B]``
-int32 (length after the append); sinks ``[Hq]`` fp32 or None.
+``[NB][Hkv][bs/8][D][8]`` bf16 (V transposed in chunks of 8 slots);
+block_table ``[B][MBS]`` int32; seq_lens ``[B]`` int32 (length after the
+append); sinks ``[Hq]`` fp32 or None.
 """
 
 from __future__ import annotations
@@ -150,11 +151,13 @@ def _check(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
 
 def _cache_dims(k_cache, v_cache, block_table, B, num_splits, variant):
     _check(k_cache, "k_cache", torch.bfloat16, 4)
-    _check(v_cache, "v_cache", torch.bfloat16, 4, k_cache.device)
+    _check(v_cache, "v_cache", torch.bfloat16, 5, k_cache.device)
     _check(block_table, "block_table", torch.int32, 2, k_cache.device)
     NB, Hkv, bs, D = k_cache.shape
-    if tuple(v_cache.shape) != (NB, Hkv, D, bs):
-        raise ValueError(f"v_cache must be [NB][Hkv][D][bs] = {(NB, Hkv, D, bs)}, "
+    if bs % 8:
+        raise ValueError(f"block_size must be a multiple of 8, got {bs}")
+    if tuple(v_cache.shape) != (NB, Hkv, bs // 8, D, 8):
+        raise ValueError(f"v_cache must be [NB][Hkv][bs/8][D][8] = {(NB, Hkv, bs // 8, D, 8)}, "
                          f"got {tuple(v_cache.shape)}")
     if block_table.shape[0] != B:
         raise ValueError("block_table must have one row per sequence")

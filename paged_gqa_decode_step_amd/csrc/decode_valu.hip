@@ -14,8 +14,9 @@
 //         it keeps in registers; one lane swap completes each score.
 //   max:  per head over the 32 slots, five lane-xor steps.
 //   P:    e^(s - m) as bf16 pairs into LDS ([head][slot pair]).
-//   PV:   lane = dimension d loads V^T[d][slots base..base+31] (the V pool
-//         is transposed inside a block, so slot pairs are adjacent bf16) and
+//   PV:   lane = dimension d loads its V^T run of slots base..base+31, four
+//         16-byte chunks (the V pool is transposed inside a block in chunks of
+//         8 slots, so slot pairs are adjacent bf16) and
 //         accumulates p . v with v_dot2_f32_bf16 against the broadcast P
 //         pairs.
 #include <math.h>
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
             const int ch = min(base + 8 * c, last_chunk);
             const int vblk = __builtin_amdgcn_readlane(tbl, (ch >> BSL) - blk0);
             const char* vp = vbase + (size_t)(unsigned)vblk * blk_stride +
-                             ((unsigned)d * bs + (ch & (bs - 1))) * 2;
+                             ((unsigned)((ch & (bs - 1)) >> 3) * kHeadDim + d) * 16;
             vr[c] = *reinterpret_cast<const u32x4_t*>(vp);
         }
 

@@ -4,7 +4,8 @@
 // also performs the KV append; full-attention layers keep a paged cache and
 // sliding-window layers a ring buffer.  Position p of sequence b lives in
 // slot p (paged) or p mod W (ring); the slot's block comes from the block
-// table.  K rows are stored [bs][D] inside a block and V rows [D][bs].  With
+// table.  Inside a block K is stored [bs][D] and V [bs/8][D][8] (transposed in
+// chunks of 8 slots).  With
 // T new tokens per sequence (a query tile; paged layers only) token t sits at
 // position L-T+t; one token is position L-1.
 //
@@ -43,7 +44,8 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
             *reinterpret_cast<u32x4_t*>(a.k_cache + head_base + (size_t)off * kHeadDim + lane * 8) =
                 k;
         }
-        a.v_cache[head_base + (size_t)lane * bs + off] = a.v_new[src + lane];
+        a.v_cache[head_base + ((size_t)(off >> 3) * kHeadDim + lane) * 8 + (off & 7)] =
+            a.v_new[src + lane];
     }
 }
 

@@ -26,7 +26,8 @@
 //     lane (head c16, q4) ends up with the scores of slots base+8*q4 .. +7;
 //   * PV reduces over slots: that same lane feeds those eight probabilities
 //     as its P^T column, and the V^T operand lane (dim row c16, q4) needs
-//     V[dim][base+8*q4 .. +7], i.e. 16 contiguous bytes of the V^T block.
+//     V[dim][base+8*q4 .. +7], i.e. 16 contiguous bytes of the V pool, which
+//     is transposed inside a block in chunks of 8 slots ([bs/8][D][8]).
 // No LDS, no barriers: cross-lane reductions of the softmax max/sum over the
 // four q4 groups use v_permlane16_swap / v_permlane32_swap.
 //
@@ -120,6 +121,15 @@ __device__ __forceinline__ u32x4_t load16(const char* p) {
 #endif
 }
 
+// V pool layout inside a (block, KV head): [bs/8][D][8], i.e. V transposed in
+// chunks of 8 slots.  A chunk is D rows of 16 bytes (one dimension's 8 slots),
+// so the PV operand (8 slots of one dimension) is one 16-byte load, and a
+// token's column (one element in each of the 64 rows) spans 8 cache lines.
+constexpr unsigned kVChunkBytes = kHeadDim * 8 * 2;
+__device__ __forceinline__ unsigned v_elem_offset(unsigned slot_in_block, unsigned dim) {
+    return ((slot_in_block >> 3) * kHeadDim + dim) * 16 + (slot_in_block & 7) * 2;
+}
+
 struct StepRegs {
     u32x4_t k[4];   // [m*2 + kstep]
     u32x4_t v[4];   // dim tile j
@@ -163,7 +173,7 @@ struct Unit {
     const int32_t* bt_row;   // block table row of the sequence
     unsigned blk_stride;     // bytes per block across all KV heads
     unsigned k_lane;         // (c16 & 3) rows + 8*q4 dims, bytes
-    unsigned v_lane;         // c16 dim rows, bytes
+    unsigned v_lane;         // c16 dim rows of a chunk, bytes
     int bs_log2;
     int num_blocks;
     int mbs;                 // entries in a block-table row
@@ -194,7 +204,7 @@ __device__ __forceinline__ Unit make_unit(const DecodeArgs& a, int b, int g, int
     u.vbase = reinterpret_cast<const char*>(a.v_cache) + (size_t)g * bs * kHeadDim * 2;
     u.bt_row = a.block_table + (size_t)b * a.mbs;
     u.k_lane = (unsigned)((u.c16 & 3) * kHeadDim + 8 * u.q4) * 2;
-    u.v_lane = (unsigned)(u.c16 * bs) * 2;
+    u.v_lane = (unsigned)u.c16 * 16;   // dim row c16 of an 8-slot chunk, bytes
     u.scale_log2 = a.scale_log2;
     u.new_slot = new_slot;
     u.rope_pos = rope_pos;
@@ -335,13 +345,13 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         const char* kp = u.kbase + (size_t)kblk * u.blk_stride +
                          ((unsigned)(kc & (bs - 1)) * kHeadDim * 2 + u.k_lane);
         const char* vp = u.vbase + (size_t)vblk * u.blk_stride +
-                         ((unsigned)(vc & (bs - 1)) * 2 + u.v_lane);
+                         ((unsigned)((vc & (bs - 1)) >> 3) * kVChunkBytes + u.v_lane);
         r.k[0] = load16(kp);
         r.k[1] = load16(kp + 64);
         r.k[2] = load16(kp + 4 * kHeadDim * 2);
         r.k[3] = load16(kp + 4 * kHeadDim * 2 + 64);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) r.v[j] = load16(vp + (size_t)j * 16 * bs * 2);
+        for (int j = 0; j < 4; ++j) r.v[j] = load16(vp + (size_t)j * 16 * 16);
     };
 
     auto compute_step = [&](int s, StepRegs& r) {
@@ -415,8 +425,9 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     // When the slot is past the first step, the store goes after the first
     // step's loads (step 1 onwards is loaded later), so any wait on the store
     // overlaps with those loads.  (The V column is one 2-byte element in each
-    // of 64 dim rows; rewriting the block's whole [D][bs] segment instead, to
-    // write whole cache lines, measured slower.)
+    // of 64 dim rows, 8 cache lines in the chunked layout; its cost grows with
+    // the lines it dirties, and no later placement of the store measured
+    // faster.)
     auto store_new = [&]() {
         const int lane = c16 + 16 * q4;
         const unsigned noff = (unsigned)(u.new_slot & (bs - 1));
@@ -441,7 +452,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         }
         // V column: lane = dim.  K row: word (lane & 31) of the 128-byte row
         // (the upper half-wave stores the same words again).
-        *reinterpret_cast<uint16_t*>(u.vstore + blk_off + ((unsigned)lane * bs + noff) * 2) = vval;
+        *reinterpret_cast<uint16_t*>(u.vstore + blk_off + v_elem_offset(noff, lane)) = vval;
         *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
             kw;
     };
@@ -460,7 +471,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
             const unsigned kw =
                 reinterpret_cast<const unsigned*>(u.kn_row + (size_t)t * u.kn_stride)[lane & 31];
             const uint16_t vv = (u.vn_row + (size_t)t * u.kn_stride)[lane];
-            *reinterpret_cast<uint16_t*>(u.vstore + off + ((unsigned)lane * bs + noff) * 2) = vv;
+            *reinterpret_cast<uint16_t*>(u.vstore + off + v_elem_offset(noff, lane)) = vv;
             *reinterpret_cast<unsigned*>(u.kstore + off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
                 kw;
         }

@@ -70,7 +70,9 @@ POISON_BITS = 0x4780   # bf16 65536.0: finite, and far outside N(0,1)
 def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int = 0,
             cap_lens=None):
     """Write the history into a K pool [NB][Hkv][bs][D], a V pool
-    [NB][Hkv][D][bs] (V transposed inside a block) and a block table.
+    [NB][Hkv][bs/c][D][c] (V transposed inside a block in chunks of
+    c = min(8, bs) slots, the library's layout for its block sizes) and a
+    block table.
 
     A full layer (window <= 0) keeps every position p < L in slot p; a ring
     layer keeps the last ``window`` positions, position p in slot p % window.
@@ -91,7 +93,8 @@ def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int
     mbs = max(nblk)
     bt = np.full((B, mbs), poison_block, dtype=np.int32)
     kp = np.full((NB, Hkv, bs, D), POISON_BITS, dtype=np.uint16)
-    vp = np.full((NB, Hkv, D, bs), POISON_BITS, dtype=np.uint16)
+    c = min(8, bs)
+    vp = np.full((NB, Hkv, bs // c, D, c), POISON_BITS, dtype=np.uint16)
     start = 0
     for b in range(B):
         bt[b, :nblk[b]] = ids[start:start + nblk[b]]
@@ -103,7 +106,7 @@ def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int
             blk = bt[b, slot // bs]
             off = slot % bs
             kp[blk, :, off, :] = h.K[b, p]
-            vp[blk, :, :, off] = h.V[b, p]
+            vp[blk, :, off // c, :, off % c] = h.V[b, p]
     return kp, vp, bt
 
 

@@ -120,7 +120,7 @@ def _tiny_layer(rng, lens, window=0, bs=16, hq=8, hkv=2):
     mbs = -(-cap // bs)
     nb = B * mbs + 1
     k = _bf16_bits(rng, (nb, hkv, bs, 64))
-    v = _bf16_bits(rng, (nb, hkv, 64, bs))
+    v = _bf16_bits(rng, (nb, hkv, bs // 8, 64, 8))     # V in chunks of 8 slots
     perm = rng.permutation(B * mbs).reshape(B, mbs).astype(np.int32)
     return dict(q=_bf16_bits(rng, (B, hq, 64)), k=k, v=v,
                 kn=_bf16_bits(rng, (B, hkv, 64)), vn=_bf16_bits(rng, (B, hkv, 64)),

@@ -98,7 +98,7 @@ def test_no_sinks_is_plain_softmax(lib):
     got = out_f64(attend(lib, layer))
     assert_parity(got, ref, "no sinks")
     # L = 1 without a sink returns v0 exactly (bf16 of it)
-    v0 = bits(layer.v_cache)[int(layer.block_table[0, 0]), :, :, 0]   # [Hkv][D]
+    v0 = bits(layer.v_cache)[int(layer.block_table[0, 0]), :, 0, :, 0]   # slot 0: [Hkv][D]
     v0 = oracle.bf16_bits_to_f64(v0)
     assert np.array_equal(got[0], np.repeat(v0, 8, axis=0))
     # sinks of -inf equal no sinks, bit for bit

@@ -75,9 +75,9 @@ def test_long_context_closed_form_q_zero(lib):
     layer.q.zero_()
     got = out_f64(attend(lib, layer))
     n = 131072
-    # mean over positions of V, per KV head: V pool is [blk][g][D][bs]
+    # mean over positions of V, per KV head: V pool is [blk][g][bs/8][D][8]
     bt = layer.block_table[0, :layer.blocks_per_seq[0]].long()
-    vsum = layer.v_cache.index_select(0, bt).double().sum(dim=(0, 3))      # [Hkv][D]
+    vsum = layer.v_cache.index_select(0, bt).double().sum(dim=(0, 2, 4))   # [Hkv][D]
     mean_v = (vsum / n).cpu().numpy()
     sig = layer.sinks.double().cpu().numpy()
     want = np.stack([mean_v[h // 8] * n / (n + math.exp(sig[h])) for h in range(64)])

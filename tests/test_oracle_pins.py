@@ -42,6 +42,13 @@ def test_append_matches_history_layout():
     pins.pin_append(oracle)
 
 
+def _v_chunked(a):
+    """The fixture's V pool [blk][kvh][d][slot] as the library's chunked layout
+    [blk][kvh][bs/c][d][c]: at the fixture's block size (2, below the chunk of
+    8) one chunk holds the whole block, so only an axis of size 1 is added."""
+    return np.asarray(a)[:, :, None]
+
+
 def _golden():
     with open(GOLDEN) as f:
         return json.load(f)
@@ -54,13 +61,13 @@ def test_hand_example_attention(layer):
     W = c.get("window", 0)
     q = np.array(g["q"], dtype=np.float64)
     out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
-                                  np.array(c["v_pool_after"], dtype=np.float64),
+                                  _v_chunked(np.array(c["v_pool_after"], dtype=np.float64)),
                                   np.array(c["block_table"]), np.array(c["seq_lens"]),
                                   np.array(g["sinks"]), W)
     np.testing.assert_allclose(out, np.array(c["expected_out"]), rtol=0, atol=1e-12)
     if "expected_out_no_sinks" in c:
         out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
-                                      np.array(c["v_pool_after"], dtype=np.float64),
+                                      _v_chunked(np.array(c["v_pool_after"], dtype=np.float64)),
                                       np.array(c["block_table"]), np.array(c["seq_lens"]),
                                       None, W)
         np.testing.assert_allclose(out, np.array(c["expected_out_no_sinks"]), rtol=0, atol=1e-12)
@@ -70,12 +77,12 @@ def test_hand_example_attention(layer):
 def test_hand_example_append(layer):
     g = _golden()
     c = g[layer]
-    k, v = oracle.kv_append(np.array(c["k_pool_before"]), np.array(c["v_pool_before"]),
+    k, v = oracle.kv_append(np.array(c["k_pool_before"]), _v_chunked(c["v_pool_before"]),
                             np.array(c["k_new"]), np.array(c["v_new"]),
                             np.array(c["block_table"]), np.array(c["seq_lens"]),
                             c.get("window", 0))
     assert np.array_equal(k, np.array(c["k_pool_after"]))
-    assert np.array_equal(v, np.array(c["v_pool_after"]))
+    assert np.array_equal(v, _v_chunked(c["v_pool_after"]))
 
 
 def test_bf16_widening_exact():
@@ -90,7 +97,7 @@ def test_bf16_widening_exact():
 def test_empty_context_and_no_sink_gives_zero():
     q = np.ones((1, 2, 4))
     kp = np.ones((2, 1, 2, 4))
-    vp = np.ones((2, 1, 4, 2))
+    vp = np.ones((2, 1, 1, 4, 2))                   # [blk][kvh][chunk][d][slot]
     out = oracle.decode_attention(q, kp, vp, np.array([[0]]), np.array([0]), None, 0)
     assert np.array_equal(out, np.zeros((1, 2, 4)))
     # a finite sink with no positions also gives 0 (the sink has no value row)
