@@ -103,3 +103,28 @@ def test_empty_context_and_no_sink_gives_zero():
     # a finite sink with no positions also gives 0 (the sink has no value row)
     out = oracle.decode_attention(q, kp, vp, np.array([[0]]), np.array([0]), np.zeros(2), 0)
     assert np.array_equal(out, np.zeros((1, 2, 4)))
+
+
+def test_pool_layout_as_documented():
+    """The oracle reads K at [blk][g][s % bs][d] and V at [blk][g][s % bs // 8][d][s % 8]
+    (the layouts the C header documents), through the block table: a pool whose
+    every element encodes its own (block, head, slot, dim) comes back row by row."""
+    from oracle import decode_step
+    NB, Hkv, bs, D = 5, 2, 16, 64
+    k = np.zeros((NB, Hkv, bs, D))
+    v = np.zeros((NB, Hkv, bs // 8, D, 8))
+    for blk in range(NB):
+        for g in range(Hkv):
+            for s in range(bs):
+                for d in range(D):
+                    code = blk * 1e6 + g * 1e5 + s * 1e3 + d
+                    k[blk, g, s, d] = code
+                    v[blk, g, s // 8, d, s % 8] = -code
+    table = np.array([[3, 0, 4]])
+    positions = [0, 7, 8, 15, 16, 33, 47]
+    for g in range(Hkv):
+        K, V = decode_step._gather(k, v, table, 0, g, positions, 0)
+        for i, p in enumerate(positions):
+            blk, s = table[0, p // bs], p % bs
+            want = blk * 1e6 + g * 1e5 + s * 1e3 + np.arange(D)
+            assert np.array_equal(K[i], want) and np.array_equal(V[i], -want), (g, p)
