@@ -43,6 +43,7 @@ sys.path.insert(0, _ROOT)
 
 PEAK_HBM = 8.0e12            # MI355X HBM3E, bytes/s
 MALL_BYTES = 256 << 20       # Infinity Cache
+ROUNDS = 5                   # further timing rounds per call, for the spread
 METRIC = "decode-attn µs/call + achieved HBM GB/s (% of peak), batch 64, 8k ctx"
 # sources of the dominant call's kernels; the committed counter summary is
 # valid only for the exact sources it was taken on
@@ -598,6 +599,13 @@ def main():
             del g
         e = dict(call=nm, us_mean=round(us, 2), bytes=b, gbps=round(b / (us * 1e-6) / 1e9, 1),
                  frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4), timing=timing)
+        if timing.startswith("eager"):
+            # spread: the same mean over ROUNDS further rounds of back-to-back calls
+            n = args.steps
+            rs = sorted(timer.mean_us(f, n) for _ in range(ROUNDS))
+            e["rounds"] = dict(rounds=ROUNDS, calls_per_round=n,
+                               us_median=round(statistics.median(rs), 2),
+                               us_min=round(rs[0], 2), us_max=round(rs[-1], 2))
         if b < 2 * MALL_BYTES:
             e["note"] = ("timed alone on one input set, which stays in the 256 MB Infinity "
                          "Cache between calls; inside the step it is read from HBM")
