@@ -650,7 +650,8 @@ def main():
             configs.append(e)
             hosts.append(h)
             print(f"# {e['config']}: {e['us']} us, {e['gbps']} GB/s", flush=True)
-        headline = configs[0]
+            if nm == "batch64_8k":
+                headline = e
         rs = rope_step_config(sa, torch, timer, dev, args.steps, args.warmup, args.variant,
                               with_oracle=oc)
         configs.append(rs)

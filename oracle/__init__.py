@@ -12,7 +12,7 @@ computes. It exists to check the HIP library, never to stand in for it:
   attention sinks, sliding window, GQA and the KV append; a paged KV cache
   for full-attention layers; a ring buffer for sliding-window layers) but
   print no formula, so each definition below is the plain textbook reading
-  of the named concept; every such reading is listed in the design doc.
+  of the named concept, stated where it is used.
 
 ``oracle.rope`` adds the decode step with the rotary position embedding of
 the new token's query and key (page 1 lists RoPE as one fused kernel), and
