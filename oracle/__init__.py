@@ -15,7 +15,7 @@ computes. It exists to check the HIP library, never to stand in for it:
   of the named concept, stated where it is used.
 
 ``oracle.rope`` adds the decode step with the rotary position embedding of
-the new token's query and key (page 1 lists RoPE as one fused kernel), and
+the new token's query and key (the SimpleLLM README lists a fused RoPE kernel), and
 ``oracle.multi_token`` the step with T > 1 causal query tokens per sequence.
 
 Pins (tests/test_oracle_*.py, ``-m "not gpu"``): a pure-Python brute force

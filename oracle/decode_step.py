@@ -3,15 +3,15 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring): the product path must
 never import this module.
 
-Sources.  Page 1 is the SimpleLLM README (shadowgraph.io/naklecha/simple-llm);
-its optimisation table has one row for the fused decode-attention kernel
+Sources.  The SimpleLLM README (shadowgraph.io/naklecha/simple-llm): its
+optimisation table has one row for the fused decode-attention kernel
 (attention sinks, sliding window, GQA and the KV append in one kernel), one
 row for the paged KV cache of full-attention layers and one row for the ring
-buffer of sliding-window layers.  Page 3 is the setup page of the
-"learn-llm-inference-from-scratch" tutorial (llminference.xinbetween.com/en/setup);
+buffer of sliding-window layers.  The setup page of the
+"learn-llm-inference-from-scratch" tutorial (llminference.xinbetween.com/en/setup):
 its file table lists chapters on the KV cache (S05), PagedAttention (S06) and
-FlashAttention (S12) without their contents.  Page 2 (a discussion thread at
-astro-solid-hn.netlify.app/stories/49693384) only remarks that GQA and
+FlashAttention (S12) without their contents.  A discussion thread
+(astro-solid-hn.netlify.app/stories/49693384) only remarks that GQA and
 sliding-window attention change an implementation a lot.  No page prints a
 formula, so the definitions here are the standard ones for the named
 concepts; the readings taken where the pages are silent are:
@@ -67,8 +67,8 @@ def bf16_bits_to_f64(x):
 # --------------------------------------------------------------------------
 
 def query_group(h: int, num_q_heads: int, num_kv_heads: int) -> int:
-    """KV head read by query head ``h`` under GQA (page 1, fused-kernel row;
-    page 2 on GQA).  Reading: contiguous groups of Hq/Hkv query heads share
+    """KV head read by query head ``h`` under GQA (SimpleLLM README, fused-kernel row;
+    the discussion thread on GQA).  Reading: contiguous groups of Hq/Hkv query heads share
     one KV head."""
     if num_q_heads % num_kv_heads:
         raise ValueError("query heads must be a multiple of KV heads")
@@ -76,7 +76,7 @@ def query_group(h: int, num_q_heads: int, num_kv_heads: int) -> int:
 
 
 def attended_positions(L: int, window: int) -> range:
-    """Positions a query at position L-1 attends to (page 1, fused-kernel row:
+    """Positions a query at position L-1 attends to (SimpleLLM README, fused-kernel row:
     sliding window).  Full attention sees [0, L); a window W > 0 sees the W
     most recent positions including the current one, [max(0, L-W), L)."""
     if window <= 0:
@@ -85,7 +85,7 @@ def attended_positions(L: int, window: int) -> range:
 
 
 def storage_slot(p, window: int):
-    """Slot that holds position p (page 1, paged-cache and ring-buffer rows).
+    """Slot that holds position p (SimpleLLM README, paged-cache and ring-buffer rows).
     A full-attention layer stores position p in slot p; a sliding-window
     layer keeps a ring of W slots and stores position p in slot p mod W.
     ``p`` may be an int or an integer array."""
@@ -94,7 +94,7 @@ def storage_slot(p, window: int):
 
 def locate(block_table, b: int, slot, block_size: int):
     """(physical block, offset) of a slot of sequence b through its block
-    table (page 1, paged-cache row; page 3, S06 PagedAttention).  ``slot``
+    table (SimpleLLM README, paged-cache row; tutorial setup page, S06 PagedAttention).  ``slot``
     may be an int or an integer array."""
     row = np.asarray(block_table)[b]
     return row[slot // block_size].astype(np.int64), slot % block_size
@@ -116,7 +116,7 @@ def _gather(k_cache, v_cache, block_table, b, g, positions, window):
 
 def _sink(sinks, h: int) -> float:
     """Sink logit of query head h; no sinks means a logit of -inf, i.e. no
-    sink at all (page 1, fused-kernel row, attention sinks)."""
+    sink at all (SimpleLLM README, fused-kernel row, attention sinks)."""
     if sinks is None:
         return -math.inf
     return float(np.asarray(sinks, dtype=np.float64)[h])
@@ -134,7 +134,7 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, sinks, window):
         out = sum_p exp(s_p - M) V_p / Z
 
     i.e. a softmax over [s_lo .. s_{L-1}, sigma_h] with the last column's
-    weight dropped (page 1, fused-kernel row; page 3, S05/S06 for the cached
+    weight dropped (SimpleLLM README, fused-kernel row; tutorial setup page, S05/S06 for the cached
     keys and values read through the block table).  With no positions and no
     sink the output is 0.
 
@@ -171,7 +171,7 @@ def partial_attention(q, k_cache, v_cache, block_table, b, h, positions, window)
     Returns ``(o, lse)`` with lse = log sum_p exp(s_p) and
     o = sum_p exp(s_p) V_p / exp(lse).  An empty subset gives (0, -inf).
     This is one split-K partition of the flash-decoding scheme that the
-    combine merges (page 3, S12 FlashAttention names the tiled softmax).
+    combine merges (tutorial setup page, S12 FlashAttention names the tiled softmax).
     """
     q = bf16_bits_to_f64(q)
     Hq, D = q.shape[1], q.shape[2]
@@ -227,7 +227,7 @@ def combine(part_o, part_lse, sinks):
 # --------------------------------------------------------------------------
 
 def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
-    """Caches after writing the new token's K and V (page 1, fused-kernel row:
+    """Caches after writing the new token's K and V (SimpleLLM README, fused-kernel row:
     the KV append; paged-cache and ring-buffer rows for where it goes).
 
     The new token of sequence b is position L-1 (L = seq_lens[b]); it goes to

@@ -1,7 +1,7 @@
 """The decode step with several new tokens per sequence (a query tile of T >
 1): TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Sources.  The tutorial's setup page (page 3) lists, beside its KV-cache and
+Sources.  The tutorial's setup page lists, beside its KV-cache and
 PagedAttention chapters, speculative decoding and chunked prefill; both read
 the paged cache with more than one new token per sequence.  No page prints the
 computation, so this is the plain causal reading:

@@ -1,12 +1,12 @@
 """Rotary position embedding of the new token's query and key, and the decode
 step with it: TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-Sources.  Page 1 (the SimpleLLM README, shadowgraph.io/naklecha/simple-llm)
-lists in its optimisation table "RoPE as one fused kernel at every batch
-size" among the decode-path kernels.  Page 3 (the setup page of the
-"learn-llm-inference-from-scratch" tutorial) warns, in its closing advice on
-running a real model, that the RoPE layout is one of the two things most
-likely to be wrong.  Neither page prints the rotation, so this module states
+Sources.  The SimpleLLM README (shadowgraph.io/naklecha/simple-llm) counts a
+fused RoPE kernel, used whatever the batch size, among the decode-path kernels
+of its optimisation table.  The setup page of the
+"learn-llm-inference-from-scratch" tutorial warns, in its closing advice on
+running a real model, that the RoPE layout is among the things most likely to
+be got wrong.  Neither page prints the rotation, so this module states
 the standard rotary embedding:
 
 * the D dims of a head vector form D/2 pairs (x1, x2), and pair i is turned
