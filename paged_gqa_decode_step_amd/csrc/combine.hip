@@ -81,12 +81,11 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hq);
     if (a.num_splits <= 8)
-        hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(64), 0, stream, a);
+        return launch(combine_kernel<1>, grid, dim3(64), 0, stream, a);
     else if (a.num_splits <= 64)
-        hipLaunchKernelGGL(combine_kernel<4>, grid, dim3(256), 0, stream, a);
+        return launch(combine_kernel<4>, grid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(combine_kernel<16>, grid, dim3(1024), 0, stream, a);
-    return hipGetLastError();
+        return launch(combine_kernel<16>, grid, dim3(1024), 0, stream, a);
 }
 
 }  // namespace sa

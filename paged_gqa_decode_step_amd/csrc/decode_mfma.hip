@@ -107,13 +107,12 @@ template <bool ROPE, bool MULTI>
 hipError_t launch_static(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hkv * a.num_splits);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL((decode_mfma_kernel<3, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_mfma_kernel<4, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL((decode_mfma_kernel<5, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL((decode_mfma_kernel<6, ROPE, MULTI>), grid, dim3(64), 0, stream, a); break;
+        case 3: return launch(decode_mfma_kernel<3, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
+        case 4: return launch(decode_mfma_kernel<4, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
+        case 5: return launch(decode_mfma_kernel<5, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
+        case 6: return launch(decode_mfma_kernel<6, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace

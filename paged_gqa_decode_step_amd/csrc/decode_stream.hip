@@ -261,13 +261,12 @@ hipError_t launch_stream_partitions(const DecodeArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)2 * a.B * sizeof(int);
     const dim3 grid(a.num_waves);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL((decode_stream_kernel<3, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
-        case 4: hipLaunchKernelGGL((decode_stream_kernel<4, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
-        case 5: hipLaunchKernelGGL((decode_stream_kernel<5, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
-        case 6: hipLaunchKernelGGL((decode_stream_kernel<6, ROPE, MULTI>), grid, dim3(64), lds, stream, a); break;
+        case 3: return launch(decode_stream_kernel<3, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
+        case 4: return launch(decode_stream_kernel<4, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
+        case 5: return launch(decode_stream_kernel<5, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
+        case 6: return launch(decode_stream_kernel<6, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace
@@ -283,12 +282,11 @@ hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stre
     const long long per_unit = (a.num_waves + units - 1) / units + 1;
     const dim3 cgrid((unsigned)a.B * a.T * a.Hq);
     if (per_unit <= kCombineChunk * 3 / 4)
-        hipLaunchKernelGGL(combine_stream_kernel<1>, cgrid, dim3(64), 0, stream, a);
+        return launch(combine_stream_kernel<1>, cgrid, dim3(64), 0, stream, a);
     else if (per_unit <= 64)
-        hipLaunchKernelGGL(combine_stream_kernel<4>, cgrid, dim3(256), 0, stream, a);
+        return launch(combine_stream_kernel<4>, cgrid, dim3(256), 0, stream, a);
     else
-        hipLaunchKernelGGL(combine_stream_kernel<16>, cgrid, dim3(1024), 0, stream, a);
-    return hipGetLastError();
+        return launch(combine_stream_kernel<16>, cgrid, dim3(1024), 0, stream, a);
 }
 
 }  // namespace sa

@@ -215,13 +215,12 @@ hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream) {
     if (a.G > kGmax) return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.B * a.Hkv * a.num_splits);
     switch (a.bs_log2) {
-        case 3: hipLaunchKernelGGL(decode_valu_kernel<3>, grid, dim3(64), 0, stream, a); break;
-        case 4: hipLaunchKernelGGL(decode_valu_kernel<4>, grid, dim3(64), 0, stream, a); break;
-        case 5: hipLaunchKernelGGL(decode_valu_kernel<5>, grid, dim3(64), 0, stream, a); break;
-        case 6: hipLaunchKernelGGL(decode_valu_kernel<6>, grid, dim3(64), 0, stream, a); break;
+        case 3: return launch(decode_valu_kernel<3>, grid, dim3(64), 0, stream, a);
+        case 4: return launch(decode_valu_kernel<4>, grid, dim3(64), 0, stream, a);
+        case 5: return launch(decode_valu_kernel<5>, grid, dim3(64), 0, stream, a);
+        case 6: return launch(decode_valu_kernel<6>, grid, dim3(64), 0, stream, a);
         default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 }  // namespace sa

@@ -52,8 +52,7 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
 }  // namespace
 
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(kv_append_kernel, dim3(a.B * a.Hkv), dim3(64), 0, stream, a);
-    return hipGetLastError();
+    return launch(kv_append_kernel, dim3(a.B * a.Hkv), dim3(64), 0, stream, a);
 }
 
 }  // namespace sa

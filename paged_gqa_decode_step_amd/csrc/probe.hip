@@ -48,9 +48,8 @@ hipError_t launch_read_probe(const void* data, size_t bytes, unsigned* sink, hip
     const size_t per_block = (size_t)kProbeThreads * kPerThread;
     size_t blocks = (n16 + per_block - 1) / per_block;
     if (blocks > kMaxProbeBlocks) blocks = kMaxProbeBlocks;    // then lanes loop
-    hipLaunchKernelGGL(read_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
-                       reinterpret_cast<const u32x4_t*>(data), n16, sink);
-    return hipGetLastError();
+    return launch(read_probe_kernel, dim3((unsigned)blocks), dim3(kProbeThreads), 0, stream,
+                  reinterpret_cast<const u32x4_t*>(data), n16, sink);
 }
 
 }  // namespace sa

@@ -6,6 +6,18 @@
 
 namespace sa {
 
+// Launch a kernel and return the status of this launch alone (hipGetLastError
+// after a triple-chevron launch would also report an error some earlier call
+// left on the calling thread).  The arguments are converted to the kernel's
+// parameter types.
+template <typename T> struct same_type { using type = T; };
+template <typename... P>
+inline hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds,
+                         hipStream_t stream, typename same_type<P>::type... args) {
+    void* ptrs[] = {static_cast<void*>(&args)...};
+    return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, stream);
+}
+
 constexpr int kHeadDim = 64;       // D handled by the kernels
 constexpr int kMaxGroup = 16;      // query columns per KV head: (query tokens) x (heads
                                    // per KV head) fill one 16-column MFMA tile
