@@ -416,3 +416,36 @@ def test_context_parallel_shards_merge(lib):
                       layer.sinks)
     torch.cuda.synchronize()
     assert_parity(out_f64(out), ref, f"{R} context shards merged")
+
+
+def test_an_earlier_hip_error_does_not_fail_a_call(lib):
+    """A call reports the status of its own launches only: an error an earlier,
+    unrelated HIP call left on the thread (an invalid device ordinal here) does
+    not turn a good call into SA_ERR_HIP."""
+    import ctypes
+    layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=[100, 2000, 7], seed=9400, device="cuda")
+    ref = oracle_attention(layer)
+    out = torch.empty_like(layer.q)
+    ws = lib.new_workspace(layer.q, layer.k_cache, layer.v_cache, layer.block_table, 0)
+    d = lib.dims_for(layer.q, layer.k_cache, layer.v_cache, layer.block_table, 0,
+                     lib.VARIANT_DEFAULT)
+    p = lambda t: ctypes.c_void_p(t.data_ptr())
+    torch.cuda.synchronize()
+    # the HIP runtime this process has loaded (the one libsa calls)
+    with open("/proc/self/maps") as f:
+        paths = sorted({ln.split()[-1] for ln in f if "libamdhip64" in ln})
+    if len(paths) != 1:
+        pytest.skip(f"{len(paths)} HIP runtimes loaded: {paths}")
+    hip = ctypes.CDLL(paths[0])
+    assert hip.hipSetDevice(ctypes.c_int(9999)) != 0          # leaves an error behind
+    st = lib.load().sa_decode_attention(p(layer.q), p(layer.k_cache), p(layer.v_cache),
+                                        p(layer.block_table), p(layer.seq_lens), p(layer.sinks),
+                                        0, p(out), ctypes.byref(d),
+                                        None if ws is None else p(ws),
+                                        0 if ws is None else ws.numel() * ws.element_size(),
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    hip.hipGetLastError()                                       # clear it again
+    assert st == 0, lib.status_string(st)
+    torch.cuda.synchronize()
+    assert_parity(out_f64(out), ref, "after an earlier HIP error")
