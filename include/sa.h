@@ -22,7 +22,9 @@
  *    inside a kernel surfaces as a HIP error at the caller's next
  *    synchronisation.
  *  - Errors are negative SA_ERR_* codes returned before anything is
- *    launched; no call aborts or throws.
+ *    launched; no call aborts or throws.  SA_ERR_HIP is the status of the
+ *    call's own launches: an error an earlier HIP call left on the thread
+ *    does not make a call fail.
  *  - q, out, k_new, v_new, k_cache, v_cache, part_o, the rotary tables and
  *    the workspace are read or written 16 bytes at a time and must be
  *    16-byte aligned (SA_ERR_INVALID_ARG otherwise).
