@@ -449,3 +449,36 @@ def test_an_earlier_hip_error_does_not_fail_a_call(lib):
     assert st == 0, lib.status_string(st)
     torch.cuda.synchronize()
     assert_parity(out_f64(out), ref, "after an earlier HIP error")
+
+
+def test_context_past_the_table_is_cut_to_its_capacity(lib):
+    """seq_lens beyond the table's capacity (max_blocks_per_seq * bs): attention
+    covers the first capacity slots, as for a sequence of that length, and the
+    append, whose slot lies past the table, writes nothing."""
+    bs = 16
+    layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=bs,
+                             lens=[20 * bs, 40, 7], seed=9500, device="cuda")
+    cap = layer.block_table.shape[1] * bs                      # 320 slots per row
+    over = torch.tensor([cap + 77, 40, 7], dtype=torch.int32, device="cuda")
+    clamped = dataclasses.replace(layer, seq_lens=torch.minimum(
+        over, torch.tensor(cap, dtype=torch.int32, device="cuda")))
+    ref = oracle_attention(clamped)
+    for v in VARIANTS:
+        out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                                   over, layer.sinks, 0, variant=v)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, f"past capacity, variant {v}")
+    # fused: sequence 0's new slot (position cap+76) is past the table: no write;
+    # the others append as usual
+    s = sub_layer(clamped, range(3))
+    lens_host = over.cpu().numpy()
+    k_ref, v_ref = oracle.kv_append(s["k"], s["v"], s["k_new"], s["v_new"], s["bt"],
+                                    np.array([0, lens_host[1], lens_host[2]]), 0)
+    out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, layer.k_cache,
+                                      layer.v_cache, layer.block_table, over, layer.sinks, 0)
+    torch.cuda.synchronize()
+    after = sub_layer(clamped, range(3))
+    assert np.array_equal(after["k"], k_ref) and np.array_equal(after["v"], v_ref)
+    ref2 = oracle.decode_attention(s["q"], k_ref, v_ref, s["bt"], np.minimum(lens_host, cap),
+                                   s["sinks"], 0)
+    assert_parity(out_f64(out), ref2, "past capacity, fused")
