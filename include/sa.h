@@ -53,9 +53,10 @@
  *  - Slot s of sequence b lives in block block_table[b][s / bs] at offset
  *    s % bs.  Only the table entries that cover attended slots are read.
  *    A context longer than max_blocks_per_seq*bs is cut to that capacity.
- *    Table entries outside [0, num_blocks) are clamped into range by the
- *    attention kernels and skipped by the append (a caller error, but
- *    never a wild access).
+ *    Table entries outside [0, num_blocks) are clamped into range for the
+ *    attention's reads, and an append whose slot's entry is outside writes
+ *    nothing, in sa_kv_append and inside the attention launch alike (a
+ *    caller error, but never a wild access).
  */
 #ifndef SA_H_
 #define SA_H_

@@ -302,19 +302,26 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int b, int g, in
 }
 
 // Block-table entries blk0 + lane of a unit, one per lane, clamped into the
-// pool (lanes past the row's end repeat its last entry; they are never used).
-// No branch around the load, so it is in flight with whatever precedes it.
-__device__ __forceinline__ int table_slice(const Unit& u, int blk0, int lane) {
+// pool for the reads (lanes past the row's end repeat its last entry; they
+// are never used), and whether the entry was inside the pool, which the
+// append's stores require: an entry outside it is a caller error that the
+// reads survive by the clamp and the append skips.  No branch around the
+// load, so it is in flight with whatever precedes it.
+struct TableSlice {
+    int blk;
+    int ok;
+};
+__device__ __forceinline__ TableSlice table_slice(const Unit& u, int blk0, int lane) {
     const int e = u.bt_row[min(blk0 + lane, u.mbs - 1)];
-    return min(max(e, 0), u.num_blocks - 1);
+    return TableSlice{min(max(e, 0), u.num_blocks - 1), (e >= 0 && e < u.num_blocks) ? 1 : 0};
 }
 
 // Attend over slots [t0, t1) of one unit (t0 a multiple of 32, t1 > t0, and
 // the run spanning at most kMaxTableSlice blocks, whose table entries tbl
-// holds), folding into st.  kword / vval: this lane's word (lane & 31) of the
+// holds, with tbl_ok their validity for the append), folding into st.  kword / vval: this lane's word (lane & 31) of the
 // new token's K row and its element `lane` of the V row.
 template <int BSL, bool ROPE, bool MULTI, int DEPTH>
-__device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl,
+__device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tbl, int tbl_ok,
                                            unsigned kword, uint16_t vval, float2 kcos,
                                            float2 ksin, int rope_style, u32x4_t qop0,
                                            u32x4_t qop1, State& st) {
@@ -330,6 +337,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     // outside the branch so the table wait is not merged into the join below
     const unsigned nblk_id =
         (unsigned)__builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl);
+    const int nblk_ok = __builtin_amdgcn_ds_bpermute(((u.new_slot >> BSL) - blk0) << 2, tbl_ok);
 
     // the 8 loads of step s (K: 2 M-tiles x 2 k-steps; V: 4 dim tiles)
     auto load_step = [&](int s, StepRegs& r) {
@@ -456,7 +464,10 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         *reinterpret_cast<unsigned*>(u.kstore + blk_off + noff * kHeadDim * 2 + 4 * (lane & 31)) =
             kw;
     };
-    const bool new_first = has_new && u.new_slot < t0 + kStepTokens;
+    // the new slot's table entry outside the pool: no append (the reads
+    // of the slot see the clamped block's contents, as for every slot)
+    const bool stores_new = has_new && nblk_ok;                  // wave-uniform
+    const bool new_first = stores_new && u.new_slot < t0 + kStepTokens;
     if (new_first) store_new();
     if (MULTI && u.appends) {
         // every new token whose slot lies in this run, before any load
@@ -466,6 +477,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
             const int lane = c16 + 16 * q4;
             const unsigned nb =
                 (unsigned)__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl);
+            if (!__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl_ok)) continue;
             const unsigned noff = (unsigned)(slot & (bs - 1));
             const size_t off = (size_t)nb * u.blk_stride;
             const unsigned kw =
@@ -487,18 +499,18 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         StepRegs A, B, C;
         if (nsteps == 1) {
             load_step(0, A);
-            if (has_new && !new_first) store_new();
+            if (stores_new && !new_first) store_new();
             compute_step(0, A);
         } else if (nsteps == 2) {
             load_step(0, A);
-            if (has_new && !new_first) store_new();
+            if (stores_new && !new_first) store_new();
             load_step(1, B);
             __builtin_amdgcn_sched_barrier(0);
             compute_step(0, A);
             compute_step(1, B);
         } else {
             load_step(0, A);
-            if (has_new && !new_first) store_new();
+            if (stores_new && !new_first) store_new();
             load_step(1, B);
             int s = 0;
             // steps s and s+1 are in flight at the top of each triple
@@ -545,7 +557,7 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     // outstanding load at the join).
     StepRegs A, B;
     load_step(0, A);
-    if (has_new && !new_first) store_new();
+    if (stores_new && !new_first) store_new();
     int s = 0;
     for (; s + 2 < nsteps; s += 2) {
         load_step(s + 1, B);
@@ -575,7 +587,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
                                        u32x4_t qop0, u32x4_t qop1, State& st) {
     constexpr int run = kMaxTableSlice << BSL;
     const int lane = u.c16 + 16 * u.q4;
-    int tbl = table_slice(u, t0 >> BSL, lane);
+    TableSlice tbl = table_slice(u, t0 >> BSL, lane);
     const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
     const uint16_t vval = u.vn_row[lane];
     // cos / sin of the pairs of this lane's new-key word (read with no branch)
@@ -593,7 +605,7 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
     }
     for (int r0 = t0;;) {
         const int r1 = min(t1, r0 + run);
-        attend_run<BSL, ROPE, MULTI, DEPTH>(u, r0, r1, tbl, kword, vval, kcos, ksin,
+        attend_run<BSL, ROPE, MULTI, DEPTH>(u, r0, r1, tbl.blk, tbl.ok, kword, vval, kcos, ksin,
                                             a.rope_style, qop0, qop1, st);
         if (r1 >= t1) break;
         r0 = r1;

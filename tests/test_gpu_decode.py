@@ -482,3 +482,46 @@ def test_context_past_the_table_is_cut_to_its_capacity(lib):
     ref2 = oracle.decode_attention(s["q"], k_ref, v_ref, s["bt"], np.minimum(lens_host, cap),
                                    s["sinks"], 0)
     assert_parity(out_f64(out), ref2, "past capacity, fused")
+
+
+def test_table_entries_outside_the_pool(lib):
+    """Block-table entries outside [0, num_blocks) are a caller error that never
+    leads to a wild access: reads clamp the entry into the pool, and an append
+    whose slot's entry is outside it writes nothing (inside the attention launch
+    as in sa_kv_append)."""
+    bs = 16
+    layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=bs,
+                             lens=[300, 200, 90], seed=9600, device="cuda")
+    NB = layer.k_cache.shape[0]
+    bad = layer.block_table.clone()
+    bad[0, 5] = -5                                   # a read of sequence 0, mid-context
+    bad[1, (200 - 1) // bs] = NB + 100               # sequence 1's new token's block
+    clipped = dataclasses.replace(layer, block_table=bad.clamp(0, NB - 1))
+    # reads: as through the clamped table
+    ref = oracle_attention(clipped)
+    for v in VARIANTS:
+        out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, bad, layer.seq_lens,
+                                   layer.sinks, 0, variant=v)
+        torch.cuda.synchronize()
+        assert_parity(out_f64(out), ref, f"entries outside the pool, variant {v}")
+    # appends: sequence 1's is skipped, the others land
+    k0 = bits(layer.k_cache)
+    v0 = bits(layer.v_cache)
+    lens = layer.seq_lens.cpu().numpy().copy()
+    skip1 = lens.copy()
+    skip1[1] = 0
+    cb = bits(clipped.block_table)
+    k_ref, v_ref = oracle.kv_append(k0, v0, bits(layer.k_new), bits(layer.v_new), cb, skip1, 0)
+    ref2 = oracle.decode_attention(bits(layer.q), k_ref, v_ref, cb, lens,
+                                   layer.sinks.cpu().numpy(), 0)
+    for v in (0, 1, 2, 4):
+        kc, vc = layer.k_cache.clone(), layer.v_cache.clone()
+        out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, kc, vc, bad,
+                                          layer.seq_lens, layer.sinks, 0, variant=v)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(kc), k_ref) and np.array_equal(bits(vc), v_ref), f"v={v}"
+        assert_parity(out_f64(out), ref2, f"fused, entries outside the pool, variant {v}")
+    kc, vc = layer.k_cache.clone(), layer.v_cache.clone()
+    lib.kv_append(layer.k_new, layer.v_new, kc, vc, bad, layer.seq_lens, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(kc), k_ref) and np.array_equal(bits(vc), v_ref)
