@@ -143,6 +143,27 @@ class Timer:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / reps
 
+    def per_call_us(self, fn, reps):
+        """Microseconds of each of reps back-to-back runs, one HIP event after
+        every run.  Each event marker adds a small gap of its own, so these
+        sit slightly above the mean of ``mean_us``; they give the spread."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(self.stream)
+        for i in range(reps):
+            fn(i)
+            ev[i + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(reps)]
+
+
+def spread(times_us):
+    """Median, 10th and 90th percentile of per-call times."""
+    q = statistics.quantiles(times_us, n=10, method="inclusive")
+    return dict(calls=len(times_us), us_median=round(statistics.median(times_us), 2),
+                us_p10=round(q[0], 2), us_p90=round(q[-1], 2))
+
 
 @contextlib.contextmanager
 def one_blas_thread():
@@ -246,6 +267,7 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
     timer.settle(call, warmup)
     us = timer.mean_us(call, steps)
     timing = "eager, back to back"
+    per_call = None
     if us < 40.0:
         per_graph = max(len(sets), 32)
         g = torch.cuda.CUDAGraph()
@@ -257,6 +279,8 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
         us = timer.mean_us(lambda _: g.replay(), reps) / per_graph
         timing = f"HIP graph of {per_graph} launches, replayed {reps} times"
         del g
+    else:
+        per_call = spread(timer.per_call_us(call, steps))
     host = note = None
     if with_oracle:
         B = first.batch
@@ -266,6 +290,7 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
         note = (f"{len(seqs)} of {B} sequences, scaled x{B / len(seqs):g}" if len(seqs) < B
                 else "every sequence")
     e = entry(label or name, "attention", us, one, input_sets=len(sets), timing=timing,
+              **({} if per_call is None else {"per_call_events": per_call}),
               splits=sa.num_splits(first.q, first.k_cache, first.v_cache, first.block_table,
                                    first.window, variant=variant))
     if note:
@@ -606,6 +631,7 @@ def main():
             e["rounds"] = dict(rounds=ROUNDS, calls_per_round=n,
                                us_median=round(statistics.median(rs), 2),
                                us_min=round(rs[0], 2), us_max=round(rs[-1], 2))
+            e["per_call_events"] = spread(timer.per_call_us(f, n))
         if b < 2 * MALL_BYTES:
             e["note"] = ("timed alone on one input set, which stays in the 256 MB Infinity "
                          "Cache between calls; inside the step it is read from HBM")

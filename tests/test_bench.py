@@ -45,3 +45,8 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300, cwd=ROOT)
     assert r.returncode != 0
     assert "one" in (r.stdout + r.stderr).lower()
+
+
+def test_spread_percentiles():
+    s = bench.spread([float(i) for i in range(1, 101)])
+    assert s == dict(calls=100, us_median=50.5, us_p10=10.9, us_p90=90.1)
