@@ -298,7 +298,7 @@ int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
 }
 
 int sa_read_bandwidth_probe(const void* data, size_t bytes, uint32_t* sink, void* stream) {
-    if (!sink || (bytes && !data) || bytes % 16) return SA_ERR_INVALID_ARG;
+    if (!sink || (bytes && !data) || bytes % 16 || !aligned16(data)) return SA_ERR_INVALID_ARG;
     if (bytes == 0) return SA_OK;
     return to_status(sa::launch_read_probe(data, bytes, sink, (hipStream_t)stream));
 }

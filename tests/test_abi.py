@@ -163,6 +163,7 @@ def test_read_probe_validates(lib):
     assert lib.sa_read_bandwidth_probe(FAKE, 16, None, None) == SA_ERR_INVALID_ARG
     assert lib.sa_read_bandwidth_probe(None, 16, sink, None) == SA_ERR_INVALID_ARG
     assert lib.sa_read_bandwidth_probe(FAKE, 20, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_bandwidth_probe(ctypes.c_void_p(0x10008), 16, sink, None) == SA_ERR_INVALID_ARG
     assert lib.sa_read_bandwidth_probe(FAKE, 0, sink, None) == 0     # nothing launched
 
 
