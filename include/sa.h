@@ -34,7 +34,9 @@
  *  - Layouts (row-major, innermost last; bf16 = IEEE bfloat16 bits):
  *      q, out          bf16 [B][Hq][D]
  *      k_new, v_new    bf16 [B][Hkv][D]
- *      k_cache         bf16 [num_blocks][Hkv][bs][D]
+ *      k_cache         bf16 [num_blocks][Hkv][2][bs][32]
+ *                      (each K row cut into two halves of 32 dims, each
+ *                       half slot-major: slot s, dim d at [d/32][s][d%32])
  *      v_cache         bf16 [num_blocks][Hkv][bs/8][D][8]
  *                      (V transposed inside a block in chunks of 8 slots:
  *                       slot s, dim d at [s/8][d][s%8])
@@ -119,8 +121,9 @@ enum {
  * KV append (SimpleLLM README, optimisation table: the fused kernel's KV
  * append; paged-cache and ring-buffer rows for where the token goes).
  * For every sequence b with L = seq_lens[b] >= 1 and every KV head g, writes
- * k_new[b][g][:] to k_cache[blk][g][off][:] and v_new[b][g][:] to
- * v_cache[blk][g][:][off], where slot s = L-1 (window <= 0) or (L-1) mod W,
+ * k_new[b][g][:] to slot off of k_cache[blk][g] and v_new[b][g][:] to slot
+ * off of v_cache[blk][g] (the layouts above), where slot s = L-1
+ * (window <= 0) or (L-1) mod W,
  * blk = block_table[b][s / bs], off = s % bs.  A bit copy: nothing else in
  * either pool changes.  Sequences with L <= 0 are skipped.
  * Uses: num_seqs, num_kv_heads, head_dim, block_size, max_blocks_per_seq,

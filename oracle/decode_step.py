@@ -26,10 +26,13 @@ concepts; the readings taken where the pages are silent are:
   stored in a ring of W slots (position p in slot p mod W); W <= 0 means a
   full-attention layer over the paged cache;
 * cache layout (the library's documented layout, restated here on its own):
-  K pool ``[num_blocks][Hkv][block_size][D]`` and V pool
-  ``[num_blocks][Hkv][block_size/c][D][c]`` (V transposed inside a block in
-  chunks of c slots: slot s, dimension d at ``[s // c][d][s % c]``; the
-  library's c is 8, the pool's last axis gives it);
+  K pool ``[num_blocks][Hkv][n][block_size][D/n]`` (each K row cut into n
+  pieces of D/n dimensions, each piece slot-major: slot s, dimension d at
+  ``[d // (D/n)][s][d % (D/n)]``; the library's n is 2, the pool's third
+  axis gives it) and V pool ``[num_blocks][Hkv][block_size/c][D][c]`` (V
+  transposed inside a block in chunks of c slots: slot s, dimension d at
+  ``[s // c][d][s % c]``; the library's c is 8, the pool's last axis gives
+  it);
   ``block_table[b][j]`` is the physical block holding slots
   ``[j*block_size, (j+1)*block_size)`` of sequence b.
 
@@ -103,8 +106,10 @@ def locate(block_table, b: int, slot, block_size: int):
 def _gather(k_cache, v_cache, block_table, b, g, positions, window):
     """K and V rows [n, D] (float64) of KV head g for the given positions."""
     p = np.asarray(positions, dtype=np.int64)
-    blks, offs = locate(block_table, b, storage_slot(p, window), k_cache.shape[2])
-    K = bf16_bits_to_f64(k_cache[blks, g, offs, :])          # [n, D]
+    blks, offs = locate(block_table, b, storage_slot(p, window), k_cache.shape[3])
+    # the row's pieces, in order (advanced indices first: [n, pieces, D/pieces])
+    D = k_cache.shape[2] * k_cache.shape[4]
+    K = bf16_bits_to_f64(k_cache[blks, g, :, offs, :]).reshape(len(p), D)    # [n, D]
     c = v_cache.shape[-1]                                    # slots per V chunk
     V = bf16_bits_to_f64(v_cache[blks, g, offs // c, :, offs % c])   # [n, D]
     return K, V
@@ -237,7 +242,7 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
     """
     k = np.array(k_cache, copy=True)
     v = np.array(v_cache, copy=True)
-    bs = k.shape[2]
+    pieces, bs = k.shape[2], k.shape[3]                      # K row pieces, block size
     Hkv = k.shape[1]
     c = v.shape[-1]                                          # slots per V chunk
     for b in range(len(seq_lens)):
@@ -247,6 +252,6 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
         blk, off = locate(block_table, b, storage_slot(L - 1, window), bs)
         blk, off = int(blk), int(off)
         for g in range(Hkv):
-            k[blk, g, off, :] = k_new[b, g, :]
+            k[blk, g, :, off, :] = np.reshape(k_new[b, g, :], (pieces, -1))
             v[blk, g, off // c, :, off % c] = v_new[b, g, :]
     return k, v

@@ -9,8 +9,9 @@ into an exception.  There is no fallback: without the built library every
 call raises.
 
 Layouts (see include/sa.h): q/out ``[B][Hq][D]`` bf16; k_new/v_new
-``[B][Hkv][D]`` bf16; k_cache ``[NB][Hkv][bs][D]`` bf16; v_cache
-``[NB][Hkv][bs/8][D][8]`` bf16 (V transposed in chunks of 8 slots);
+``[B][Hkv][D]`` bf16; k_cache ``[NB][Hkv][2][bs][D/2]`` bf16 (each K row
+in two halves, each half slot-major); v_cache ``[NB][Hkv][bs/8][D][8]`` bf16
+(V transposed in chunks of 8 slots);
 block_table ``[B][MBS]`` int32; seq_lens ``[B]`` int32 (length after the
 append); sinks ``[Hq]`` fp32 or None.
 """
@@ -150,10 +151,13 @@ def _check(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
 
 
 def _cache_dims(k_cache, v_cache, block_table, B, num_splits, variant):
-    _check(k_cache, "k_cache", torch.bfloat16, 4)
+    _check(k_cache, "k_cache", torch.bfloat16, 5)
     _check(v_cache, "v_cache", torch.bfloat16, 5, k_cache.device)
     _check(block_table, "block_table", torch.int32, 2, k_cache.device)
-    NB, Hkv, bs, D = k_cache.shape
+    NB, Hkv, halves, bs, half = k_cache.shape
+    D = halves * half
+    if halves != 2:
+        raise ValueError(f"k_cache must be [NB][Hkv][2][bs][D/2], got {tuple(k_cache.shape)}")
     if bs % 8:
         raise ValueError(f"block_size must be a multiple of 8, got {bs}")
     if tuple(v_cache.shape) != (NB, Hkv, bs // 8, D, 8):

@@ -9,7 +9,8 @@
 //
 // Per 32-slot step, for the G <= 8 query heads of one KV group:
 //   QK^T: lane l = (slot t = l/2, half = l%2) loads its half K row (64 B;
-//         the wave reads 32 full 128-byte rows, fully coalesced) and forms
+//         the K pool keeps each half of a block's rows slot-major, [2][bs][32],
+//         so the wave reads whole cache lines) and forms
 //         the eight half dot products with v_dot2_f32_bf16 from the queries
 //         it keeps in registers; one lane swap completes each score.
 //   max:  per head over the 32 slots, five lane-xor steps.
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(64) void decode_valu_kernel(const DecodeArgs a) {
         const int slot = min(base + t, t1 - 1);
         const unsigned kblk = (unsigned)__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl);
         const char* kp = kbase + (size_t)kblk * blk_stride +
-                         ((unsigned)(slot & (bs - 1)) * kHeadDim + 32 * half) * 2;
+                         ((unsigned)(half * bs + (slot & (bs - 1))) * 32) * 2;
         u32x4_t kr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) kr[i] = *reinterpret_cast<const u32x4_t*>(kp + 16 * i);

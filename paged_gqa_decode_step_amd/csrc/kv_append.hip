@@ -4,15 +4,15 @@
 // also performs the KV append; full-attention layers keep a paged cache and
 // sliding-window layers a ring buffer.  Position p of sequence b lives in
 // slot p (paged) or p mod W (ring); the slot's block comes from the block
-// table.  Inside a block K is stored [bs][D] and V [bs/8][D][8] (transposed in
-// chunks of 8 slots).  With
-// T new tokens per sequence (a query tile; paged layers only) token t sits at
-// position L-T+t; one token is position L-1.
+// table.  Inside a block K is stored [2][bs][32] (each half of a row, 32
+// dimensions, slot-major) and V [bs/8][D][8] (transposed in chunks of 8
+// slots).  With T new tokens per sequence (a query tile; paged layers only)
+// token t sits at position L-T+t; one token is position L-1.
 //
 // One 64-lane wavefront per (sequence, KV head), token by token: lanes 0..7
-// store the 128-byte K row as eight 16-byte stores; all 64 lanes store one
-// 2-byte V element each (the V column of the slot).  A bit copy; no
-// arithmetic on the values.
+// store the K row as eight 16-byte stores (four per 64-byte half); all 64
+// lanes store one 2-byte V element each (the V column of the slot).  A bit
+// copy; no arithmetic on the values.
 #include "sa_internal.h"
 
 namespace sa {
@@ -41,8 +41,9 @@ __global__ __launch_bounds__(64) void kv_append_kernel(const AppendArgs a) {
         const size_t src = (((size_t)b * a.T + t) * a.Hkv + g) * kHeadDim;
         if (lane < kHeadDim / 8) {
             const u32x4_t k = *reinterpret_cast<const u32x4_t*>(a.k_new + src + lane * 8);
-            *reinterpret_cast<u32x4_t*>(a.k_cache + head_base + (size_t)off * kHeadDim + lane * 8) =
-                k;
+            // dims 8*lane .. +7: half lane/4, 16-byte piece lane%4 of it
+            const size_t kdst = head_base + ((size_t)(lane >> 2) * bs + off) * 32 + (lane & 3) * 8;
+            *reinterpret_cast<u32x4_t*>(a.k_cache + kdst) = k;
         }
         a.v_cache[head_base + ((size_t)(off >> 3) * kHeadDim + lane) * 8 + (off & 7)] =
             a.v_new[src + lane];

@@ -6,8 +6,9 @@ What is drawn (no attention arithmetic happens here):
 * ``k_new``, ``v_new``  bf16 ``[B][Hkv][D]``, N(0,1) times ``scale``;
 * ``sinks``   fp32 ``[Hq]``, N(0,1) (or ``None``);
 * the KV pools, bf16, every element N(0,1) times ``scale``:
-  ``k_cache [NB][Hkv][bs][D]`` and ``v_cache [NB][Hkv][bs/8][D][8]`` (the
-  library's layout: V transposed inside a block in chunks of 8 slots);
+  ``k_cache [NB][Hkv][2][bs][D/2]`` and ``v_cache [NB][Hkv][bs/8][D][8]``
+  (the library's layouts: each K row in two halves of D/2 dimensions, each
+  half slot-major; V transposed inside a block in chunks of 8 slots);
 * ``block_table`` int32 ``[B][MBS]``: each sequence owns ``ceil(cap/bs)``
   distinct physical blocks (``cap`` = its capacity in tokens for a paged
   layer, the window for a ring layer), drawn from a seeded permutation of the
@@ -150,7 +151,8 @@ def make_layer(*, batch, q_heads, kv_heads, head_dim=64, block_size=16, lens,
     elems = nb * kv_heads * block_size * head_dim
     dev = torch.device(device)
     pool_dev = dev if (dev.type != "cpu" and elems > _DEVICE_POOL_ELEMS) else torch.device("cpu")
-    k_cache = _normal_bf16((nb, kv_heads, block_size, head_dim), s[1], scale, pool_dev)
+    # K rows in two halves, each half slot-major; V in chunks of 8 slots
+    k_cache = _normal_bf16((nb, kv_heads, 2, block_size, head_dim // 2), s[1], scale, pool_dev)
     v_cache = _normal_bf16((nb, kv_heads, block_size // 8, head_dim, 8), s[2], scale, pool_dev)
     k_cache[poison_block].fill_(poison)
     v_cache[poison_block].fill_(-poison)

@@ -93,5 +93,5 @@ def poison_tails(layer: synth.Layer, value_bits: int = 0x7FC0):
         return
     bi = torch.as_tensor(blks, device=kv.device)
     oi = torch.as_tensor(offs, device=kv.device)
-    kv[bi, :, oi, :] = int(val)
+    kv[bi, :, :, oi, :] = int(val)
     vv[bi, :, oi // 8, :, oi % 8] = int(val)

@@ -69,10 +69,10 @@ POISON_BITS = 0x4780   # bf16 65536.0: finite, and far outside N(0,1)
 
 def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int = 0,
             cap_lens=None):
-    """Write the history into a K pool [NB][Hkv][bs][D], a V pool
-    [NB][Hkv][bs/c][D][c] (V transposed inside a block in chunks of
-    c = min(8, bs) slots, the library's layout for its block sizes) and a
-    block table.
+    """Write the history into a K pool [NB][Hkv][2][bs][D/2] (each K row in two
+    halves, each half slot-major), a V pool [NB][Hkv][bs/c][D][c] (V
+    transposed inside a block in chunks of c = min(8, bs) slots), the
+    library's layouts for its block sizes, and a block table.
 
     A full layer (window <= 0) keeps every position p < L in slot p; a ring
     layer keeps the last ``window`` positions, position p in slot p % window.
@@ -92,7 +92,8 @@ def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int
     poison_block = int(ids[used])
     mbs = max(nblk)
     bt = np.full((B, mbs), poison_block, dtype=np.int32)
-    kp = np.full((NB, Hkv, bs, D), POISON_BITS, dtype=np.uint16)
+    n = 2 if D % 2 == 0 else 1                 # K row pieces (the library's 2)
+    kp = np.full((NB, Hkv, n, bs, D // n), POISON_BITS, dtype=np.uint16)
     c = min(8, bs)
     vp = np.full((NB, Hkv, bs // c, D, c), POISON_BITS, dtype=np.uint16)
     start = 0
@@ -105,7 +106,7 @@ def lay_out(h: History, window: int, bs: int, table: str = "shuffled", seed: int
             slot = p if window <= 0 else p % window
             blk = bt[b, slot // bs]
             off = slot % bs
-            kp[blk, :, off, :] = h.K[b, p]
+            kp[blk, :, :, off, :] = h.K[b, p].reshape(Hkv, n, D // n)
             vp[blk, :, off // c, :, off % c] = h.V[b, p]
     return kp, vp, bt
 

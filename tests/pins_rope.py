@@ -119,7 +119,7 @@ def _tiny_layer(rng, lens, window=0, bs=16, hq=8, hkv=2):
     cap = max(max(lens), window if window > 0 else 0, 1)
     mbs = -(-cap // bs)
     nb = B * mbs + 1
-    k = _bf16_bits(rng, (nb, hkv, bs, 64))
+    k = _bf16_bits(rng, (nb, hkv, 2, bs, 32))          # K rows in two halves
     v = _bf16_bits(rng, (nb, hkv, bs // 8, 64, 8))     # V in chunks of 8 slots
     perm = rng.permutation(B * mbs).reshape(B, mbs).astype(np.int32)
     return dict(q=_bf16_bits(rng, (B, hq, 64)), k=k, v=v,

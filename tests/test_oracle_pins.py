@@ -42,6 +42,13 @@ def test_append_matches_history_layout():
     pins.pin_append(oracle)
 
 
+def _k_rows(a):
+    """The fixture's K pool [blk][kvh][slot][d] in the documented piece layout
+    [blk][kvh][n][bs][D/n] with n = 1 (a row in one piece): an axis of size 1
+    is added."""
+    return np.asarray(a)[:, :, None]
+
+
 def _v_chunked(a):
     """The fixture's V pool [blk][kvh][d][slot] as the library's chunked layout
     [blk][kvh][bs/c][d][c]: at the fixture's block size (2, below the chunk of
@@ -60,13 +67,13 @@ def test_hand_example_attention(layer):
     c = g[layer]
     W = c.get("window", 0)
     q = np.array(g["q"], dtype=np.float64)
-    out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
+    out = oracle.decode_attention(q, _k_rows(np.array(c["k_pool_after"], dtype=np.float64)),
                                   _v_chunked(np.array(c["v_pool_after"], dtype=np.float64)),
                                   np.array(c["block_table"]), np.array(c["seq_lens"]),
                                   np.array(g["sinks"]), W)
     np.testing.assert_allclose(out, np.array(c["expected_out"]), rtol=0, atol=1e-12)
     if "expected_out_no_sinks" in c:
-        out = oracle.decode_attention(q, np.array(c["k_pool_after"], dtype=np.float64),
+        out = oracle.decode_attention(q, _k_rows(np.array(c["k_pool_after"], dtype=np.float64)),
                                       _v_chunked(np.array(c["v_pool_after"], dtype=np.float64)),
                                       np.array(c["block_table"]), np.array(c["seq_lens"]),
                                       None, W)
@@ -77,11 +84,11 @@ def test_hand_example_attention(layer):
 def test_hand_example_append(layer):
     g = _golden()
     c = g[layer]
-    k, v = oracle.kv_append(np.array(c["k_pool_before"]), _v_chunked(c["v_pool_before"]),
+    k, v = oracle.kv_append(_k_rows(c["k_pool_before"]), _v_chunked(c["v_pool_before"]),
                             np.array(c["k_new"]), np.array(c["v_new"]),
                             np.array(c["block_table"]), np.array(c["seq_lens"]),
                             c.get("window", 0))
-    assert np.array_equal(k, np.array(c["k_pool_after"]))
+    assert np.array_equal(k, _k_rows(c["k_pool_after"]))
     assert np.array_equal(v, _v_chunked(c["v_pool_after"]))
 
 
@@ -96,7 +103,7 @@ def test_bf16_widening_exact():
 
 def test_empty_context_and_no_sink_gives_zero():
     q = np.ones((1, 2, 4))
-    kp = np.ones((2, 1, 2, 4))
+    kp = np.ones((2, 1, 2, 2, 2))                   # [blk][kvh][half][slot][d % 2]
     vp = np.ones((2, 1, 1, 4, 2))                   # [blk][kvh][chunk][d][slot]
     out = oracle.decode_attention(q, kp, vp, np.array([[0]]), np.array([0]), None, 0)
     assert np.array_equal(out, np.zeros((1, 2, 4)))
@@ -106,19 +113,20 @@ def test_empty_context_and_no_sink_gives_zero():
 
 
 def test_pool_layout_as_documented():
-    """The oracle reads K at [blk][g][s % bs][d] and V at [blk][g][s % bs // 8][d][s % 8]
-    (the layouts the C header documents), through the block table: a pool whose
-    every element encodes its own (block, head, slot, dim) comes back row by row."""
+    """The oracle reads K at [blk][g][d // 32][s % bs][d % 32] and V at
+    [blk][g][s % bs // 8][d][s % 8] (the layouts the C header documents),
+    through the block table: a pool whose every element encodes its own
+    (block, head, slot, dim) comes back row by row."""
     from oracle import decode_step
     NB, Hkv, bs, D = 5, 2, 16, 64
-    k = np.zeros((NB, Hkv, bs, D))
+    k = np.zeros((NB, Hkv, 2, bs, D // 2))
     v = np.zeros((NB, Hkv, bs // 8, D, 8))
     for blk in range(NB):
         for g in range(Hkv):
             for s in range(bs):
                 for d in range(D):
                     code = blk * 1e6 + g * 1e5 + s * 1e3 + d
-                    k[blk, g, s, d] = code
+                    k[blk, g, d // 32, s, d % 32] = code
                     v[blk, g, s // 8, d, s % 8] = -code
     table = np.array([[3, 0, 4]])
     positions = [0, 7, 8, 15, 16, 33, 47]

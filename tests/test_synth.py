@@ -29,7 +29,7 @@ def test_shapes_tables_and_poison():
     L = [1, 16, 17, 100]
     lay = synth.make_layer(batch=4, q_heads=8, kv_heads=2, head_dim=64, block_size=16,
                            lens=L, seed=3)
-    assert lay.k_cache.shape == (lay.num_blocks, 2, 16, 64)
+    assert lay.k_cache.shape == (lay.num_blocks, 2, 2, 16, 32)    # [NB][Hkv][2][bs][D/2]
     assert lay.v_cache.shape == (lay.num_blocks, 2, 2, 64, 8)      # [NB][Hkv][bs/8][D][8]
     assert lay.k_cache.dtype == torch.bfloat16 and lay.sinks.dtype == torch.float32
     assert lay.blocks_per_seq == [1, 1, 2, 7]
