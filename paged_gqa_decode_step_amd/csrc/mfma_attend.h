@@ -65,6 +65,10 @@ typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// How far (log2 units) a head's running max may rise above the reference max
+// of the online softmax before the state is rescaled: probabilities stay below
+// 2^8, far inside the range of the fp32 sums and of the bf16 P operand.
+constexpr float kRescaleSlack = 8.0f;
 
 // x[l] op x[l ^ 16] and x[l] op x[l ^ 32] without LDS: each swap gives every
 // lane its own value in one result and its partner's in the other.
@@ -382,11 +386,11 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         s0 = mfma(r.k[1], qop1, s0);
         s1 = mfma(r.k[2], qop0, s1);
         s1 = mfma(r.k[3], qop1, s1);
-        float t[8];
+        float t[8];          // q.k; the scale joins in the exponent's fused multiply-add
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            t[i] = s0[i] * u.scale_log2;
-            t[4 + i] = s1[i] * u.scale_log2;
+            t[i] = s0[i];
+            t[4 + i] = s1[i];
         }
         const int tok = t0 + (s << 5) + (q4 << 3);   // slot of t[0] on this lane
         if (MULTI && tok + 8 > col_lim) {             // the column's causal limit
@@ -412,29 +416,35 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         }
         float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])),
                          fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
-        mx = max_xor32(max_xor16(mx));
-        // finite whenever this step or an earlier one of the state had a live
-        // slot; a wholly masked step on a fresh state keeps m = -inf and must
-        // not rescale (exp2(-inf - -inf) would be NaN)
-        const float m_new = fmaxf(st.m, mx);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(st.m - m_ref);
+        mx = max_xor32(max_xor16(mx)) * u.scale_log2;   // the scale is positive
+        // The reference max st.m moves, and the state is rescaled, only when
+        // some head's max rises more than kRescaleSlack above it; otherwise
+        // the probabilities stay below 2^kRescaleSlack and most steps skip the
+        // rescale (a wave-uniform branch).  A fresh state (m = -inf) takes the
+        // first live step's max; a wholly masked step on a fresh state keeps
+        // m = -inf and its probabilities are exp2(-inf) = 0.
+        if (__builtin_amdgcn_ballot_w64(mx > st.m + kRescaleSlack) != 0) {
+            const float m_new = fmaxf(st.m, mx);
+            const float alpha =
+                __builtin_amdgcn_exp2f(st.m - (m_new == -INFINITY ? 0.f : m_new));
+            st.l *= alpha;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) st.acc[j] *= alpha;
+            st.m = m_new;
+        }
+        const float m_ref = st.m == -INFINITY ? 0.f : st.m;
         float p[8];
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            p[e] = __builtin_amdgcn_exp2f(t[e] - m_ref);
+            p[e] = __builtin_amdgcn_exp2f(fmaf(t[e], u.scale_log2, -m_ref));
             psum += p[e];
         }
-        st.l = st.l * alpha + psum;
+        st.l += psum;
         const u32x4_t pop = {pack_bf16(p[0], p[1]), pack_bf16(p[2], p[3]),
                              pack_bf16(p[4], p[5]), pack_bf16(p[6], p[7])};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            st.acc[j] *= alpha;
-            st.acc[j] = mfma(r.v[j], pop, st.acc[j]);
-        }
-        st.m = m_new;
+        for (int j = 0; j < 4; ++j) st.acc[j] = mfma(r.v[j], pop, st.acc[j]);
     };
 
     // The append (the fused form of the KV append): the one run that holds
