@@ -18,9 +18,11 @@
  *    The library never allocates, frees or synchronises; it keeps no
  *    global mutable state and is safe to call from several host threads.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
- *    null stream).  A return of SA_OK means the work was enqueued; a fault
- *    inside a kernel surfaces as a HIP error at the caller's next
- *    synchronisation.
+ *    null stream of the calling thread's current HIP device).  A return of
+ *    SA_OK means the work was enqueued; a fault inside a kernel surfaces as a
+ *    HIP error at the caller's next synchronisation.  Launches go to the
+ *    calling thread's current device, which must be the device of `stream`
+ *    and of every pointer passed.
  *  - Errors are negative SA_ERR_* codes returned before anything is
  *    launched; no call aborts or throws.  SA_ERR_HIP is the status of the
  *    call's own launches: an error an earlier HIP call left on the thread

@@ -127,12 +127,21 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> ctypes.c_void_p:
+def _stream(stream, device) -> ctypes.c_void_p:
+    """The stream to launch on: the given one, else torch's current stream of
+    the tensors' device."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(device)
     if isinstance(stream, torch.cuda.Stream):
         return ctypes.c_void_p(stream.cuda_stream)
     return ctypes.c_void_p(int(stream))
+
+
+def _on(device):
+    """The tensors' device made current around a call: the library launches on
+    the calling thread's current HIP device (torch's default stream is that
+    device's null stream)."""
+    return torch.cuda.device(device)
 
 
 def _check(t: torch.Tensor, name: str, dtype, ndim: int, device=None):
@@ -217,9 +226,10 @@ def kv_append(k_new, v_new, k_cache, v_cache, block_table, seq_lens, window=0, s
     if seq_lens.shape[0] != B:
         raise ValueError("seq_lens must have one entry per sequence")
     d.num_q_heads = d.num_kv_heads
-    st = load().sa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
-                             _ptr(block_table), _ptr(seq_lens), int(window),
-                             ctypes.byref(d), _stream(stream))
+    with _on(k_cache.device):
+        st = load().sa_kv_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(block_table), _ptr(seq_lens), int(window),
+                                 ctypes.byref(d), _stream(stream, k_cache.device))
     _raise(st, "sa_kv_append")
 
 
@@ -271,9 +281,11 @@ def decode_attention(q, k_cache, v_cache, block_table, seq_lens, sinks=None, win
     if workspace is None:
         workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load().sa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                    _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out),
-                                    ctypes.byref(d), _ptr(workspace), ws_bytes, _stream(stream))
+    with _on(dev):
+        st = load().sa_decode_attention(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                        _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out),
+                                        ctypes.byref(d), _ptr(workspace), ws_bytes,
+                                        _stream(stream, dev))
     _raise(st, "sa_decode_attention")
     return out
 
@@ -300,10 +312,11 @@ def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_
     if workspace is None:
         workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = load().sa_decode_attention_append(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d), _ptr(workspace),
-        ws_bytes, _stream(stream))
+    with _on(dev):
+        st = load().sa_decode_attention_append(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d), _ptr(workspace),
+            ws_bytes, _stream(stream, dev))
     _raise(st, "sa_decode_attention_append")
     return out
 
@@ -338,10 +351,11 @@ def decode_attention_append_rope(q, k_new, v_new, k_cache, v_cache, block_table,
         workspace = new_workspace(q, k_cache, v_cache, block_table, window, num_splits, variant)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     r = Rope(cos_table.data_ptr(), sin_table.data_ptr(), cos_table.shape[0], int(style))
-    st = load().sa_decode_attention_append_rope(
-        _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-        _ptr(seq_lens), _ptr(sinks), int(window), ctypes.byref(r), _ptr(out), ctypes.byref(d),
-        _ptr(workspace), ws_bytes, _stream(stream))
+    with _on(dev):
+        st = load().sa_decode_attention_append_rope(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(sinks), int(window), ctypes.byref(r), _ptr(out), ctypes.byref(d),
+            _ptr(workspace), ws_bytes, _stream(stream, dev))
     _raise(st, "sa_decode_attention_append_rope")
     return out
 
@@ -364,9 +378,10 @@ def decode_partials(q, k_cache, v_cache, block_table, seq_lens, window=0, num_sp
     _check(part_lse, "part_lse", torch.float32, len(lead) + 1, dev)
     if tuple(part_o.shape) != lead + (S, D) or tuple(part_lse.shape) != lead + (S,):
         raise ValueError(f"partials must be {list(lead)}+[{S}][D] and {list(lead)}+[{S}]")
-    st = load().sa_decode_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
-                                   _ptr(seq_lens), int(window), _ptr(part_o), _ptr(part_lse),
-                                   ctypes.byref(d), _stream(stream))
+    with _on(dev):
+        st = load().sa_decode_partials(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                       _ptr(seq_lens), int(window), _ptr(part_o), _ptr(part_lse),
+                                       ctypes.byref(d), _stream(stream, dev))
     _raise(st, "sa_decode_partials")
     return part_o, part_lse
 
@@ -398,8 +413,9 @@ def combine(part_o, part_lse, sinks=None, out=None, stream=None):
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, 3, dev)
     d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0, 0)
-    st = load().sa_combine(_ptr(part_o), _ptr(part_lse), _ptr(sinks), int(S), _ptr(out),
-                           ctypes.byref(d), _stream(stream))
+    with _on(dev):
+        st = load().sa_combine(_ptr(part_o), _ptr(part_lse), _ptr(sinks), int(S), _ptr(out),
+                               ctypes.byref(d), _stream(stream, dev))
     _raise(st, "sa_combine")
     return out
 
@@ -412,5 +428,7 @@ def read_bandwidth_probe(data, sink, stream=None):
         raise ValueError("data must be a contiguous GPU tensor")
     _check(sink, "sink", torch.int32, 1, data.device)
     nbytes = data.numel() * data.element_size()
-    st = load().sa_read_bandwidth_probe(_ptr(data), nbytes, _ptr(sink), _stream(stream))
+    with _on(data.device):
+        st = load().sa_read_bandwidth_probe(_ptr(data), nbytes, _ptr(sink),
+                                            _stream(stream, data.device))
     _raise(st, "sa_read_bandwidth_probe")
