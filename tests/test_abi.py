@@ -239,3 +239,18 @@ def test_misaligned_pointers_rejected(lib):
         args[i] = odd
         assert lib.sa_decode_attention_append(*args) == SA_ERR_INVALID_ARG, i
     assert lib.sa_decode_partials(ok, ok, ok, ok, ok, 0, odd, ok, d, None) == SA_ERR_INVALID_ARG
+
+
+def test_binding_checks_the_pool_layouts():
+    """The binding refuses a K pool of plain rows ([NB][Hkv][bs][D]) before any
+    call: the documented layout is [NB][Hkv][2][bs][D/2].  (On host tensors the
+    shape test comes before the device test; a pool of the right shape on the
+    host is refused for its device.)"""
+    import pytest
+    import torch
+    bt = torch.zeros(1, 1, dtype=torch.int32)
+    v = torch.zeros(3, 2, 2, 64, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k_cache must have 5 dims"):
+        sa._cache_dims(torch.zeros(3, 2, 16, 64, dtype=torch.bfloat16), v, bt, 1, 0, 0)
+    with pytest.raises(ValueError, match="k_cache must be on a GPU device"):
+        sa._cache_dims(torch.zeros(3, 2, 2, 16, 32, dtype=torch.bfloat16), v, bt, 1, 0, 0)
