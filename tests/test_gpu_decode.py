@@ -525,3 +525,43 @@ def test_table_entries_outside_the_pool(lib):
     lib.kv_append(layer.k_new, layer.v_new, kc, vc, bad, layer.seq_lens, 0)
     torch.cuda.synchronize()
     assert np.array_equal(bits(kc), k_ref) and np.array_equal(bits(vc), v_ref)
+
+
+def _set_keys(layer, b, rows):
+    """Write K rows [n][Hkv][D] for positions 0..n-1 of sequence b into the
+    pool (test-side layout arithmetic: position p in block table[b][p // bs] at
+    slot p % bs; a K row as two halves of 32 dims)."""
+    bs = layer.block_size
+    p = torch.arange(rows.shape[0], device=rows.device)
+    blks = layer.block_table[b].to(torch.long)[p // bs]
+    n, hkv, d = rows.shape
+    layer.k_cache[blks, :, :, p % bs, :] = rows.reshape(n, hkv, 2, d // 2).to(torch.bfloat16)
+
+
+def test_running_max_rises_jumps_and_falls(lib):
+    """Score profiles that move the online softmax's running max in every way:
+    a steady climb far past 2^8 (many rescales), one late jump to a single
+    position that then dominates the output (and a lower peak after it), a
+    staircase of rises each below 2^8 (probabilities up to that size between
+    rescales), and a steady fall.  In each KV group the first query head gets the profile
+    exactly (keys along its query), the others a random fraction of it."""
+    lens = [3000, 3000, 2000, 700]
+    layer = synth.make_layer(batch=4, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
+                             lens=lens, seed=720, device="cuda")
+    G = 8
+    for b, L in enumerate(lens):
+        p = torch.arange(L, device="cuda", dtype=torch.float32)
+        s = [60.0 * p / L,                                     # climb
+             torch.where(p == 2500, 40.0, torch.where(p == 2900, 35.0, 0.0)),  # late jump
+             4.0 * torch.floor(p / 200),                       # staircase below 2^8
+             30.0 - 60.0 * p / L][b]                           # fall
+        rows = torch.empty(L, 2, 64, device="cuda")
+        for g in range(2):
+            q0 = layer.q[b, g * G].float()
+            rows[:, g] = s[:, None] * 8.0 * q0[None, :] / float(q0 @ q0)
+        _set_keys(layer, b, rows)
+    ref = oracle_attention(layer)
+    for v in VARIANTS:
+        for S in (0, 3):
+            assert_parity(out_f64(attend(lib, layer, num_splits=S, variant=v)), ref,
+                          f"running max v={v} S={S}")
