@@ -19,6 +19,9 @@ Reported (one JSON line):
                of K and V rows).
   roofline     the dominant call (the full-layer attention), timed with HIP
                events on the stream it runs on, back to back.
+  The ring layer's pools (18 MB) would stay in the 256 MB Infinity Cache from
+  one step to the next; it rotates over enough input sets that every step reads
+  it from HBM, as a model with many layers would.
   cpu_baseline the fp64 oracle on this host, on the same step.
   configs      every synthetic configuration: GPU us per call, GB/s and
                fraction of peak, next to the oracle's seconds on a bounded
@@ -86,14 +89,14 @@ def load_traffic():
 # workloads
 # ---------------------------------------------------------------------------
 
-def ragged_layers(device, seed_offset=0):
+def ragged_layers(device, seed_offset=0, windows=(0, 128)):
     import synth
     c = synth.CONFIGS["batch64_ragged"]
     lens = synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + 1
     common = dict(batch=c["batch"], q_heads=c["q_heads"], kv_heads=c["kv_heads"],
                   head_dim=c["head_dim"], block_size=c["block_size"], lens=lens, device=device)
-    return [synth.make_layer(window=0, seed=c["seed"] + 10 + seed_offset, **common),
-            synth.make_layer(window=128, seed=c["seed"] + 20 + seed_offset, **common)]
+    seed = {0: c["seed"] + 10, 128: c["seed"] + 20}
+    return [synth.make_layer(window=w, seed=seed[w] + seed_offset, **common) for w in windows]
 
 
 def make_workload(name, device, seed_offset=0):
@@ -559,6 +562,18 @@ def main():
     timer = Timer(torch, stream)
 
     layers = make_workload(args.workload, dev)
+    # a layer whose pools would stay in the 256 MB Infinity Cache between steps
+    # (the ring layer) rotates over input sets, so that every step reads it
+    # from HBM as a model's many layers would
+    rotations = []
+    for L in layers:
+        pool = L.k_cache.numel() * 4
+        n = 1 if pool > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // max(pool, 1)))
+        rot = [L]
+        if n > 1 and args.workload == "batch64_ragged":
+            rot += [ragged_layers(dev, seed_offset=101 * i, windows=(L.window,))[0]
+                    for i in range(1, n)]
+        rotations.append(rot)
     outs = [torch.empty_like(L.q) for L in layers]
     wss = [sa.new_workspace(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
                             variant=args.variant) for L in layers]
@@ -569,45 +584,49 @@ def main():
 
     # (name, bytes, thunk) in step order; launches go to torch's current stream,
     # which is the timed stream (and the capture stream while a graph records)
+    # call i of a layer uses input set i mod (its sets); the sets share lengths
+    # and shapes, so bytes, splits and workspace are those of the first
     calls = []
-    for L, o, ws in zip(layers, outs, wss):
-        lens = L.seq_lens.cpu().tolist()
+    for L0, rot, o, ws in zip(layers, rotations, outs, wss):
+        lens = L0.seq_lens.cpu().tolist()
         if fused:
             # the append happens inside the attention launch (rewriting the
             # same slot with the same row on every repeat)
-            calls.append((f"append+attention(w={L.window})",
-                          attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim) +
-                          append_bytes(L.batch),
-                          lambda _=0, L=L, o=o, ws=ws: sa.decode_attention_append(
+            calls.append((f"append+attention(w={L0.window})",
+                          attn_bytes(lens, L0.window, L0.q_heads, L0.kv_heads, L0.head_dim) +
+                          append_bytes(L0.batch),
+                          lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention_append(
                               L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
                               L.seq_lens, L.sinks, L.window, out=o, workspace=ws,
-                              variant=args.variant)))
+                              variant=args.variant))(rot[i % len(rot)]), len(rot)))
             continue
         if with_append:
-            calls.append((f"append(w={L.window})", append_bytes(L.batch),
-                          lambda _=0, L=L: sa.kv_append(L.k_new, L.v_new, L.k_cache, L.v_cache,
-                                                        L.block_table, L.seq_lens, L.window)))
-        calls.append((f"attention(w={L.window})",
-                       attn_bytes(lens, L.window, L.q_heads, L.kv_heads, L.head_dim),
-                       lambda _=0, L=L, o=o, ws=ws: sa.decode_attention(
+            calls.append((f"append(w={L0.window})", append_bytes(L0.batch),
+                          lambda i=0, rot=rot: (lambda L: sa.kv_append(
+                              L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                              L.seq_lens, L.window))(rot[i % len(rot)]), len(rot)))
+        calls.append((f"attention(w={L0.window})",
+                       attn_bytes(lens, L0.window, L0.q_heads, L0.kv_heads, L0.head_dim),
+                       lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention(
                            L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
-                           L.window, out=o, workspace=ws, variant=args.variant)))
+                           L.window, out=o, workspace=ws, variant=args.variant))(
+                           rot[i % len(rot)]), len(rot)))
 
-    def step(_=0):
-        for _, _, f in calls:
-            f()
+    def step(i=0):
+        for _, _, f, _ in calls:
+            f(i)
 
     print(f"# workload {args.workload}: splits {splits}, warmup {args.warmup}", flush=True)
     timer.settle(step, args.warmup)
 
     # the timed region: exactly K steps, events at its two ends only
     ms_per_step = timer.mean_us(step, args.steps) / 1e3
-    step_bytes = sum(b for _, b, _ in calls)
+    step_bytes = sum(b for _, b, _, _ in calls)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # per-call means: each call alone, K times back to back
     per_call = []
-    for nm, b, f in calls:
+    for nm, b, f, nsets in calls:
         timer.settle(f, args.warmup)
         us = timer.mean_us(f, args.steps)
         timing = "eager, back to back"
@@ -623,7 +642,8 @@ def main():
             timing = f"HIP graph of {per_graph} launches, replayed {reps} times"
             del g
         e = dict(call=nm, us_mean=round(us, 2), bytes=b, gbps=round(b / (us * 1e-6) / 1e9, 1),
-                 frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4), timing=timing)
+                 frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4), timing=timing,
+                 input_sets=nsets)
         if timing.startswith("eager"):
             # spread: the same mean over ROUNDS further rounds of back-to-back calls
             n = args.steps
@@ -632,9 +652,9 @@ def main():
                                us_median=round(statistics.median(rs), 2),
                                us_min=round(rs[0], 2), us_max=round(rs[-1], 2))
             e["per_call_events"] = spread(timer.per_call_us(f, n))
-        if b < 2 * MALL_BYTES:
-            e["note"] = ("timed alone on one input set, which stays in the 256 MB Infinity "
-                         "Cache between calls; inside the step it is read from HBM")
+        if nsets > 1:
+            e["note"] = (f"{nsets} input sets in rotation (in the step too), so no call finds "
+                         "its inputs in the 256 MB Infinity Cache")
         per_call.append(e)
         print(f"# {nm}: {us:.2f} us, {b / (us * 1e-6) / 1e9:.1f} GB/s", flush=True)
 
@@ -657,7 +677,7 @@ def main():
           flush=True)
 
     main_hosts = None if args.no_cpu_baseline else [host_inputs(L) for L in layers]
-    del calls, layers, outs, wss
+    del calls, layers, rotations, outs, wss
     torch.cuda.empty_cache()
 
     configs = []
