@@ -520,6 +520,57 @@ def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=
 
 # ---------------------------------------------------------------------------
 
+SWEEP_POINTS = ([(B, 8192) for B in (1, 2, 4, 8, 16, 32, 64, 128, 256)] +
+                [(64, L) for L in (512, 1024, 2048, 4096, 16384, 32768)])
+
+
+def sweep(sa, torch, timer, dev, steps, warmup):
+    """The fused step (append inside the attention launch) of a paged full
+    layer, 64 query / 8 KV heads, D 64, bs 16, uniform context L (after the
+    append), over SWEEP_POINTS.  Inputs that would fit the Infinity Cache
+    rotate over enough sets that every call reads HBM."""
+    import synth
+    for B, L in SWEEP_POINTS:
+        mk = lambda i: synth.make_layer(batch=B, q_heads=64, kv_heads=8, head_dim=64,    # noqa: E731
+                                        block_size=16, lens=[L] * B, seed=3000 + 101 * i,
+                                        device=dev)
+        first = mk(0)
+        pool = first.k_cache.numel() * 4
+        nsets = 1 if pool > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // max(pool, 1)))
+        sets = [first] + [mk(i) for i in range(1, nsets)]
+        outs = [torch.empty_like(x.q) for x in sets]
+        ws = sa.new_workspace(first.q, first.k_cache, first.v_cache, first.block_table, 0)
+
+        def call(i):
+            x = sets[i % len(sets)]
+            sa.decode_attention_append(x.q, x.k_new, x.v_new, x.k_cache, x.v_cache,
+                                       x.block_table, x.seq_lens, x.sinks, 0,
+                                       out=outs[i % len(sets)], workspace=ws)
+        timer.settle(call, warmup)
+        us = timer.mean_us(call, steps)
+        timing = "eager, back to back"
+        if us < 40.0:
+            g = torch.cuda.CUDAGraph()
+            per_graph = max(len(sets), 32)
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
+                    call(i)
+            reps = max(2, steps // 10)
+            timer.settle(lambda _: g.replay(), reps)
+            us = timer.mean_us(lambda _: g.replay(), reps) / per_graph
+            timing = f"HIP graph of {per_graph} launches"
+            del g
+        nbytes = attn_bytes([L] * B, 0) + append_bytes(B)
+        print(json.dumps(dict(batch=B, context=L, us=round(us, 2), bytes=nbytes,
+                              gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                              frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4),
+                              splits=sa.num_splits(first.q, first.k_cache, first.v_cache,
+                                                   first.block_table, 0),
+                              input_sets=len(sets), timing=timing)), flush=True)
+        del sets, outs, ws, first
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -536,6 +587,9 @@ def main():
                          "inside it")
     ap.add_argument("--graph", action="store_true",
                     help="replay the decode loop's step from a HIP graph")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the fused step of a paged full layer over a grid of batch "
+                         "sizes and context lengths (one JSON line per point) and exit")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, three times, and exit: the "
                          "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -560,6 +614,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     timer = Timer(torch, stream)
+    if args.sweep:
+        sweep(sa, torch, timer, dev, args.steps, args.warmup)
+        return
 
     layers = make_workload(args.workload, dev)
     # a layer whose pools would stay in the 256 MB Infinity Cache between steps

@@ -134,9 +134,17 @@ Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
         case SA_VARIANT_VALU:
             return Mode::kStatic;
         default:
-            // one static partition needs no merge at all; beyond that the
-            // balanced kernel keeps every compute unit equally busy
+            // one static partition needs no merge at all; nor is the balanced
+            // kernel worth its fixed costs (the length scan, the merge's
+            // segment records) for two partitions a unit on a grid of at most
+            // one wavefront per SIMD, where every partition runs at once
+            // (measured on MI355X: 1-3 us faster for batches of up to 512 units
+            // with contexts of 1025-2048, uniform or ragged; at more units, or
+            // at four partitions, the balanced kernel was faster); beyond that
+            // the balanced kernel keeps every compute unit equally busy
             if (d->num_splits > 0 || p.splits == 1 || !fits_stream) return Mode::kStatic;
+            if (p.splits == 2 && (long)d->num_seqs * d->num_kv_heads * 2 <= kStreamWaves)
+                return Mode::kStatic;
             return Mode::kBalanced;
     }
 }

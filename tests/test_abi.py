@@ -254,3 +254,19 @@ def test_binding_checks_the_pool_layouts():
         sa._cache_dims(torch.zeros(3, 2, 16, 64, dtype=torch.bfloat16), v, bt, 1, 0, 0)
     with pytest.raises(ValueError, match="k_cache must be on a GPU device"):
         sa._cache_dims(torch.zeros(3, 2, 2, 16, 32, dtype=torch.bfloat16), v, bt, 1, 0, 0)
+
+
+def test_two_partitions_on_a_small_grid_take_the_static_split(lib):
+    """Two partitions per (sequence, KV head) with at most 512 such units run
+    the static split (its workspace holds two partials for every output row);
+    with more units, the balanced kernel (two partial slots per wavefront of
+    1024)."""
+    def ws(B):
+        d = good_dims(num_seqs=B, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=128)
+        assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == 2
+        return lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
+    counters = (1 << 16) * 4
+    rows = 64 * 64 * 2                                   # B x Hq x S
+    assert ws(64) == counters + rows * 64 * 4 + rows * 4 + 64 * 8 * 2 * 4
+    rows = 1024 * 2 * 8                                  # wavefronts x 2 slots x G
+    assert ws(128) == counters + rows * 64 * 4 + rows * 4 + 128 * 8 * 2 * 4
