@@ -154,8 +154,9 @@ struct StepRegs {
 };
 
 // Online-softmax state of one wavefront: acc[j] lane (head c16, q4) holds dims
-// 16j + 4*q4 .. +3 of that head; m is the running max (log2 domain, equal on
-// the head's four lanes); l is this lane's share of the running sum.
+// 16j + 4*q4 .. +3 of that head; m is the reference max of the exponents
+// (log2 domain, equal on the head's four lanes; at most kRescaleSlack below the
+// running max); l is this lane's share of the running sum.
 struct State {
     f32x4_t acc[4];
     float m;
