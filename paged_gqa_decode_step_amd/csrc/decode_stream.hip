@@ -170,10 +170,11 @@ void decode_stream_kernel(const DecodeArgs a) {
 // by one wavefront, and units with no step, were written by the partition
 // kernel.  Two memory round trips: the unit's segment record, then its
 // partials, CHUNK segments per wavefront at a time with every load issued
-// before any is used (indices past the last segment are clamped to it and
-// weighted 0, so no load sits under a branch).  The one-wavefront form, for
-// units spread over a few wavefronts, takes 8 at a time: the clamped loads
-// and weights of a 16-wide chunk measured 0.4-1.3 us slower on batch-64 calls.
+// before any is used (a chunk's loads sit under wave-uniform conditions with
+// no wait between them, so a chunk is one round trip; past the last segment
+// nothing is read and the weight is 0).  The one-wavefront form, for units
+// spread over a few wavefronts, takes 8 at a time: a 16-wide chunk measured
+// 0.4-1.3 us slower on batch-64 calls.
 constexpr int kCombineChunk = 16;
 constexpr int kCombineChunkOneWave = 8;
 
@@ -206,10 +207,14 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
         float l[CHUNK], o[CHUNK];
 #pragma unroll
         for (int j = 0; j < CHUNK; ++j) {
-            const int k = min(k0 + j, nseg - 1);
-            const size_t sl = (size_t)(k == 0 ? first : 2 * (i0 + k)) * ncol + hl;
-            l[j] = a.part_lse[sl];
-            o[j] = a.part_o[sl * kHeadDim + lane];
+            const int k = k0 + j;
+            l[j] = -INFINITY;
+            o[j] = 0.f;
+            if (k < nseg) {           // wave-uniform; the loads still all go out first
+                const size_t sl = (size_t)(k == 0 ? first : 2 * (i0 + k)) * ncol + hl;
+                l[j] = a.part_lse[sl];
+                o[j] = a.part_o[sl * kHeadDim + lane];
+            }
         }
         float M2 = M;
 #pragma unroll
