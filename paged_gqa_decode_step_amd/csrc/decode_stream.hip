@@ -172,11 +172,12 @@ void decode_stream_kernel(const DecodeArgs a) {
 // partials, CHUNK segments per wavefront at a time with every load issued
 // before any is used (a chunk's loads sit under wave-uniform conditions with
 // no wait between them, so a chunk is one round trip; past the last segment
-// nothing is read and the weight is 0).  The one-wavefront form, for units
-// spread over a few wavefronts, takes 8 at a time: a 16-wide chunk measured
-// 0.4-1.3 us slower on batch-64 calls.
-constexpr int kCombineChunk = 16;
-constexpr int kCombineChunkOneWave = 8;
+// nothing is read and the weight is 0).  Chunks of 8: 16-wide chunks measured
+// 0.4-1.3 us slower on batch-64 calls and 0.4 us on batch-1 and -8 calls.
+constexpr int kCombineChunk = 8;
+// segments per unit (if lengths were equal) up to which one wavefront merges
+// a (b, h) row
+constexpr int kOneWaveMergeSegs = 12;
 
 template <int WAVES, int CHUNK>
 __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const DecodeArgs a) {
@@ -289,9 +290,8 @@ hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stre
     const long long units = (long long)a.B * a.Hkv;
     const long long per_unit = (a.num_waves + units - 1) / units + 1;
     const dim3 cgrid((unsigned)a.B * a.T * a.Hq);
-    if (per_unit <= kCombineChunk * 3 / 4)
-        return launch(combine_stream_kernel<1, kCombineChunkOneWave>, cgrid, dim3(64), 0, stream,
-                      a);
+    if (per_unit <= kOneWaveMergeSegs)
+        return launch(combine_stream_kernel<1, kCombineChunk>, cgrid, dim3(64), 0, stream, a);
     else if (per_unit <= 64)
         return launch(combine_stream_kernel<4, kCombineChunk>, cgrid, dim3(256), 0, stream, a);
     else
