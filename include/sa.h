@@ -251,9 +251,10 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
  * Log-sum-exp combine of num_splits partials per (b, h) with the sink:
  *     M = max(max_j part_lse[b][h][j], sigma_h)
  *     out[b][h] = sum_j e^(lse_j - M) part_o[b][h][j] / (sum_j e^(lse_j - M) + e^(sigma_h - M))
- * rounded to bf16; partials with lse = -inf are skipped (their part_o is
- * never read); 0 where nothing remains.  Uses num_seqs, num_q_heads and
- * head_dim of dims.
+ * rounded to bf16; partials with lse = -inf carry no weight (whatever their
+ * part_o holds, NaN included, never reaches out; the whole [B][Hq][S][D]
+ * part_o must still be allocated); 0 where nothing remains.  Uses num_seqs,
+ * num_q_heads and head_dim of dims.
  */
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
                int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream);

@@ -6,11 +6,13 @@
 // from): every partition j of (b, h) leaves o_j (its own softmax average of
 // V) and lse_j = log sum e^s over its slots.  With M = max(max_j lse_j, sigma_h)
 //     out = sum_j e^(lse_j - M) o_j / (sum_j e^(lse_j - M) + e^(sigma_h - M)).
-// Partials with lse = -inf (empty partitions) carry no weight and are never
-// read.
+// Partials with lse = -inf (empty partitions) carry no weight: whatever their
+// o holds (NaN included) never reaches the output.
 //
-// One workgroup per (b, h) with WAVES wavefronts: every wavefront finds M over
-// all partials (lanes stride over them), then merges the partials j = w,
+// One workgroup per (b, h).  Up to kOneWaveSplits partitions, one wavefront
+// reads every lse and o row at once (lane = dimension) and merges them: one
+// round trip.  Beyond that, WAVES wavefronts: every wavefront finds M over all
+// partials (lanes stride over them), then merges the partials j = w,
 // w + WAVES, ... with lane = dimension, so each partial row is one coalesced
 // 256-byte load and WAVES rows are in flight at once; the per-wave sums meet
 // in LDS.
@@ -22,6 +24,7 @@ namespace sa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kOneWaveSplits = 8;   // partitions up to which one wavefront merges a row
 
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
@@ -40,6 +43,40 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
     const int S = a.num_splits;
     const float* lse = a.part_lse + (size_t)bh * S;
     const float sig = a.sinks ? a.sinks[h] : -INFINITY;
+
+    if (WAVES == 1) {
+        // S <= kOneWaveSplits: every partial's lse (the row's, so the same on
+        // all lanes) and o are read at once, one round trip; an empty
+        // partition's o is read but selected away, whatever its bits
+        float l[kOneWaveSplits], o[kOneWaveSplits];
+#pragma unroll
+        for (int j = 0; j < kOneWaveSplits; ++j) {
+            l[j] = -INFINITY;
+            o[j] = 0.f;
+            if (j < S) {
+                l[j] = lse[j];
+                o[j] = a.part_o[((size_t)bh * S + j) * kHeadDim + lane];
+            }
+        }
+        float M = sig;
+#pragma unroll
+        for (int j = 0; j < kOneWaveSplits; ++j) M = fmaxf(M, l[j]);
+        if (M == -INFINITY) {                   // nothing attended and no sink
+            a.out[(size_t)bh * kHeadDim + lane] = 0;
+            return;
+        }
+        float num = 0.f, den = __builtin_amdgcn_exp2f((sig - M) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < kOneWaveSplits; ++j) {
+            const bool live = l[j] != -INFINITY;
+            const float wt = live ? __builtin_amdgcn_exp2f((l[j] - M) * kLog2e) : 0.f;
+            den += wt;
+            num += live ? wt * o[j] : 0.f;
+        }
+        const __bf16 ob = (__bf16)(num / den);
+        a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, ob);
+        return;
+    }
 
     float M = sig;
     for (int j = lane; j < S; j += 64) M = fmaxf(M, lse[j]);
@@ -80,7 +117,7 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hq);
-    if (a.num_splits <= 8)
+    if (a.num_splits <= kOneWaveSplits)
         return launch(combine_kernel<1>, grid, dim3(64), 0, stream, a);
     else if (a.num_splits <= 64)
         return launch(combine_kernel<4>, grid, dim3(256), 0, stream, a);

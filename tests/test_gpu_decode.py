@@ -215,16 +215,19 @@ def test_partials_and_combine_entry_points(lib):
     assert_parity(out_f64(out), oracle_attention(layer), "partials + combine")
 
 
-def test_combine_alone(lib):
+@pytest.mark.parametrize("S", [2, 8, 9])         # one-wavefront merge up to 8, then 4 waves
+def test_combine_alone(lib, S):
     """sa_combine on random partials, some empty (-inf), against the oracle."""
     g = torch.Generator().manual_seed(5)
-    B, Hq, S, D = 3, 8, 9, 64
+    B, Hq, D = 3, 8, 64
     po = torch.randn(B, Hq, S, D, generator=g)
     pl = torch.randn(B, Hq, S, generator=g) * 4
-    pl[0, :, 3] = -math.inf
+    e = min(3, S - 1)
+    pl[0, :, e] = -math.inf
     pl[1, 2, :] = -math.inf            # a head with nothing: only the sink
     pl[2, 5, :] = -math.inf
-    po[0, :, 3] = float("nan")        # never read
+    po[0, :, e] = float("nan")        # an empty partition's o never reaches out
+    po[2, 5, :] = float("nan")
     sinks = torch.randn(Hq, generator=g)
     ref = oracle.combine(po.numpy(), pl.numpy(), sinks.numpy())
     out = lib.combine(po.cuda(), pl.cuda(), sinks.cuda())
