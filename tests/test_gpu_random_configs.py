@@ -32,7 +32,7 @@ def draw(seed):
                 variant=variant, splits=splits)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(100))
 def test_random_configuration(lib, seed):
     c = draw(seed)
     layer = synth.make_layer(batch=c["B"], q_heads=c["hkv"] * c["G"], kv_heads=c["hkv"],
@@ -61,7 +61,7 @@ def test_random_configuration(lib, seed):
     assert_parity(out_f64(out2), ref2, tag + " (fused)")
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_query_tile(lib, seed):
     """T causal query tokens per sequence (T*G <= 16), paged layers, the fused
     append of the tile's rows included."""
@@ -91,7 +91,7 @@ def test_random_query_tile(lib, seed):
     assert_parity(out_f64(out), ref, tag)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_rope_step(lib, seed):
     """The step with the rotary embedding fused in: either pairing, paged or
     ring, positions past the tables' end included."""
