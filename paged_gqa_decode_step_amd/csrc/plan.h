@@ -50,6 +50,9 @@ constexpr long kWaveQuantum = 512;
 constexpr long kMaxSegsPerUnit = 128;
 constexpr long kMinStreamSteps = 8;
 constexpr int kMaxStreamSeqs = 2048;
+// partitions per row up to which the static combine reads every partial at
+// once (its one-wavefront form)
+constexpr int kStaticMergeSplits = 8;
 
 struct Plan {
     int32_t splits;
@@ -133,19 +136,23 @@ Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
         case SA_VARIANT_MFMA_TWO_PASS:
         case SA_VARIANT_VALU:
             return Mode::kStatic;
-        default:
+        default: {
             // one static partition needs no merge at all; nor is the balanced
             // kernel worth its fixed costs (the length scan, the merge's
-            // segment records) for two partitions a unit on a grid of at most
-            // one wavefront per SIMD, where every partition runs at once
-            // (measured on MI355X: 1-3 us faster for batches of up to 512 units
-            // with contexts of 1025-2048, uniform or ragged; at more units, or
-            // at four partitions, the balanced kernel was faster); beyond that
-            // the balanced kernel keeps every compute unit equally busy
+            // segment records) when the static grid holds between half and one
+            // wavefront per SIMD and the static merge reads every partial of a
+            // row in one round trip (at most kStaticMergeSplits): then every
+            // partition runs at once (measured on MI355X: 0.2-2.8 us faster
+            // from batch 8 x 8192 to 64 x 2048, uniform or ragged; with fewer
+            // partitions than that the GPU is not filled, with more the
+            // balanced kernel's even split wins); beyond that the balanced
+            // kernel keeps every compute unit equally busy
             if (d->num_splits > 0 || p.splits == 1 || !fits_stream) return Mode::kStatic;
-            if (p.splits == 2 && (long)d->num_seqs * d->num_kv_heads * 2 <= kStreamWaves)
+            const long parts = (long)d->num_seqs * d->num_kv_heads * p.splits;
+            if (p.splits <= kStaticMergeSplits && parts >= kStreamWaves / 2 && parts <= kStreamWaves)
                 return Mode::kStatic;
             return Mode::kBalanced;
+        }
     }
 }
 

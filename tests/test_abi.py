@@ -256,17 +256,26 @@ def test_binding_checks_the_pool_layouts():
         sa._cache_dims(torch.zeros(3, 2, 2, 16, 32, dtype=torch.bfloat16), v, bt, 1, 0, 0)
 
 
-def test_two_partitions_on_a_small_grid_take_the_static_split(lib):
-    """Two partitions per (sequence, KV head) with at most 512 such units run
-    the static split (its workspace holds two partials for every output row);
-    with more units, the balanced kernel (two partial slots per wavefront of
-    1024)."""
-    def ws(B):
-        d = good_dims(num_seqs=B, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=128)
-        assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == 2
-        return lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
+def test_small_grids_of_few_partitions_take_the_static_split(lib):
+    """A static grid of 512 to 1024 partitions with at most 8 per (sequence,
+    KV head) runs the static split (its workspace holds S partials for every
+    output row); a smaller or larger grid, the balanced kernel (two partial
+    slots per wavefront of 1024)."""
     counters = (1 << 16) * 4
-    rows = 64 * 64 * 2                                   # B x Hq x S
-    assert ws(64) == counters + rows * 64 * 4 + rows * 4 + 64 * 8 * 2 * 4
-    rows = 1024 * 2 * 8                                  # wavefronts x 2 slots x G
-    assert ws(128) == counters + rows * 64 * 4 + rows * 4 + 128 * 8 * 2 * 4
+
+    def ws(B, mbs, S):
+        d = good_dims(num_seqs=B, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=mbs)
+        assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == S
+        return lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
+
+    def static(B, S):
+        rows = B * 64 * S                                # B x Hq x S
+        return counters + rows * 64 * 4 + rows * 4 + B * 8 * 2 * 4
+
+    def balanced(B):
+        rows = 1024 * 2 * 8                              # wavefronts x 2 slots x G
+        return counters + rows * 64 * 4 + rows * 4 + B * 8 * 2 * 4
+    assert ws(64, 128, 2) == static(64, 2)               # 1024 partitions
+    assert ws(8, 512, 8) == static(8, 8)                 # 512
+    assert ws(128, 128, 2) == balanced(128)              # 2048
+    assert ws(4, 512, 8) == balanced(4)                  # 256
