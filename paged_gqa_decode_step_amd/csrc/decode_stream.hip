@@ -42,8 +42,10 @@ __device__ __forceinline__ long long wave_start(long long i, long long T, long l
 // kernel reads as "done".
 __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, int lane) {
     for (int g = 0; g < a.Hkv; ++g) write_zero(a, b, g, lane);
-    if (lane < a.Hkv) {
-        int* seg = a.unit_seg + 2 * (b * a.Hkv + lane);
+    // one record per KV head, however many heads there are (the workspace is
+    // reused from call to call, so a record left out would be a stale one)
+    for (int g = lane; g < a.Hkv; g += 64) {
+        int* seg = a.unit_seg + 2 * (b * a.Hkv + g);
         seg[0] = 2 * i;
         seg[1] = i;
     }
