@@ -237,8 +237,11 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
 
     The new token of sequence b is position L-1 (L = seq_lens[b]); it goes to
     slot storage_slot(L-1, window) through the block table, for every KV head.
-    Sequences with L <= 0 append nothing.  Returns modified copies; the copy
-    is a bit copy, so any dtype (e.g. bf16 bits as uint16) works.
+    Sequences with L <= 0 append nothing, and neither does a sequence whose
+    slot lies past its table row (slot >= entries x block_size: a length past
+    the table's capacity, a caller error the library documents as writing
+    nothing).  Returns modified copies; the copy is a bit copy, so any dtype
+    (e.g. bf16 bits as uint16) works.
     """
     k = np.array(k_cache, copy=True)
     v = np.array(v_cache, copy=True)
@@ -249,7 +252,10 @@ def kv_append(k_cache, v_cache, k_new, v_new, block_table, seq_lens, window):
         L = int(seq_lens[b])
         if L <= 0:
             continue
-        blk, off = locate(block_table, b, storage_slot(L - 1, window), bs)
+        slot = storage_slot(L - 1, window)
+        if slot // bs >= np.asarray(block_table).shape[1]:
+            continue                                         # past the table: no write
+        blk, off = locate(block_table, b, slot, bs)
         blk, off = int(blk), int(off)
         for g in range(Hkv):
             k[blk, g, :, off, :] = np.reshape(k_new[b, g, :], (pieces, -1))

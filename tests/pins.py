@@ -359,3 +359,28 @@ def pin_append(oracle, seed=61):
         # in a ring the new token overwrites the position that has just left
         # the window, so the pool after is exactly the layout of h
         assert np.array_equal(ka, kp1) and np.array_equal(va, vp1), f"append W={W} bs={bs}"
+
+
+def pin_append_past_capacity(oracle, seed=67):
+    """A sequence whose new token's slot lies past its table row (a length
+    beyond the table's capacity, which the library documents as appending
+    nothing) leaves the pools untouched; the other sequences of the same call
+    append as usual.  Checked against the history layouts, bit for bit."""
+    D = 64
+    for bs in (8, 16):
+        h = make_history(seed, 3, 4, 2, D, [20, 30, 9])
+        before = dataclasses.replace(h, lens=h.lens - 1)
+        kp0, vp0, bt = lay_out(before, 0, bs, seed=5, cap_lens=h.lens)
+        kp1, vp1, _ = lay_out(h, 0, bs, seed=5)
+        cap = bt.shape[1] * bs
+        k_new = np.stack([h.K[b, h.lens[b] - 1] for b in range(3)])
+        v_new = np.stack([h.V[b, h.lens[b] - 1] for b in range(3)])
+        for L1 in (cap + 1, cap + 8, 3 * cap + 5):
+            lens = h.lens.copy()
+            lens[1] = L1                             # new slot L1-1 >= cap: past the row
+            ka, va = oracle.kv_append(kp0, vp0, k_new, v_new, bt, lens, 0)
+            own1 = bt[1, :-(-int(h.lens[1]) // bs)]  # sequence 1's blocks: as before
+            want_k, want_v = kp1.copy(), vp1.copy()
+            want_k[own1], want_v[own1] = kp0[own1], vp0[own1]
+            assert np.array_equal(ka, want_k) and np.array_equal(va, want_v), \
+                f"append past capacity bs={bs} L={L1}"

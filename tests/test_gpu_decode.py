@@ -296,6 +296,35 @@ def test_empty_sequences_zeroed_over_stale_state(lib, lens):
         assert_parity(out_f64(out), ref, f"lens={lens} v={v}")
 
 
+@pytest.mark.parametrize("lens", [[1800, 0], [0, 1800], [0, 0]])
+def test_empty_sequences_with_more_than_64_kv_heads(lib, lens):
+    """128 KV heads of one query head each: an empty sequence must leave a
+    "done" record for every one of its units, not only for the first 64, when
+    the workspace was dirtied by a call in which those units were spread over
+    several wavefronts (a stale record would merge that call's partials over
+    the zeros)."""
+    B, H = 2, 128
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    dirty = synth.make_layer(batch=B, q_heads=H, kv_heads=H, head_dim=64, block_size=16,
+                             lens=[2000] * B, capacity=[2048] * B, seed=1310, device="cuda")
+    layer = synth.make_layer(batch=B, q_heads=H, kv_heads=H, head_dim=64, block_size=16,
+                             lens=lens, capacity=[2048] * B, seed=1410 + sum(lens) // 7,
+                             device="cuda")
+    ref = oracle_attention(layer)
+    for v in (0, 4):
+        lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
+                             dirty.seq_lens, dirty.sinks, 0, workspace=ws, variant=v)
+        out = torch.full_like(layer.q, float("nan"))
+        lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                             layer.seq_lens, layer.sinks, 0, out=out, workspace=ws, variant=v)
+        torch.cuda.synchronize()
+        got = out_f64(out)
+        assert_parity(got, ref, f"lens={lens} v={v}")
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert not got[b].any(), f"sequence {b} is empty: all zeros (v={v})"
+
+
 @pytest.mark.parametrize("W", [0, 128])
 def test_short_sequences_under_a_large_capacity(lib, W):
     """Tables sized for long contexts (8192 slots) holding short ones: the
@@ -471,12 +500,12 @@ def test_context_past_the_table_is_cut_to_its_capacity(lib):
                                    over, layer.sinks, 0, variant=v)
         torch.cuda.synchronize()
         assert_parity(out_f64(out), ref, f"past capacity, variant {v}")
-    # fused: sequence 0's new slot (position cap+76) is past the table: no write;
-    # the others append as usual
+    # fused: sequence 0's new slot (position cap+76) is past the table: the
+    # oracle's append writes nothing there either; the others append as usual
     s = sub_layer(clamped, range(3))
     lens_host = over.cpu().numpy()
     k_ref, v_ref = oracle.kv_append(s["k"], s["v"], s["k_new"], s["v_new"], s["bt"],
-                                    np.array([0, lens_host[1], lens_host[2]]), 0)
+                                    lens_host, 0)
     out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, layer.k_cache,
                                       layer.v_cache, layer.block_table, over, layer.sinks, 0)
     torch.cuda.synchronize()

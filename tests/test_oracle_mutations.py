@@ -14,7 +14,8 @@ from oracle import decode_step
 import pins
 
 ALL_PINS = [pins.pin_brute_force, pins.pin_sdpa, pins.pin_closed_forms,
-            pins.pin_invariants, pins.pin_combine, pins.pin_append]
+            pins.pin_invariants, pins.pin_combine, pins.pin_append,
+            pins.pin_append_past_capacity]
 
 
 def _some_pin_fails(monkeypatch_ctx):
@@ -34,6 +35,7 @@ def _mutations():
     orig_gather = decode_step._gather
     orig_positions = decode_step.attended_positions
     orig_locate = decode_step.locate
+    orig_append = decode_step.kv_append
 
     def group_modulo(h, hq, hkv):                 # interleaved instead of contiguous groups
         return h % hkv
@@ -59,6 +61,12 @@ def _mutations():
         blk, off = orig_locate(block_table, b, slot, bs)
         return blk, off * 0
 
+    def append_clamped_to_capacity(k_cache, v_cache, k_new, v_new, block_table, seq_lens, w):
+        # a slot past the table row written to the row's last slot instead of skipped
+        cap = np.asarray(block_table).shape[1] * k_cache.shape[3]
+        lens = [min(int(L), cap) if w <= 0 else int(L) for L in seq_lens]
+        return orig_append(k_cache, v_cache, k_new, v_new, block_table, lens, w)
+
     return [
         ("query_group", group_modulo),
         ("storage_slot", slot_off_by_one),
@@ -67,6 +75,7 @@ def _mutations():
         ("_gather", v_untransposed),
         ("attended_positions", window_excludes_current),
         ("locate", offset_from_block_start),
+        ("kv_append", append_clamped_to_capacity),
     ]
 
 

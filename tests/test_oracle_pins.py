@@ -42,6 +42,10 @@ def test_append_matches_history_layout():
     pins.pin_append(oracle)
 
 
+def test_append_past_capacity_writes_nothing():
+    pins.pin_append_past_capacity(oracle)
+
+
 def _k_rows(a):
     """The fixture's K pool [blk][kvh][slot][d] in the documented piece layout
     [blk][kvh][n][bs][D/n] with n = 1 (a row in one piece): an axis of size 1
