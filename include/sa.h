@@ -42,6 +42,12 @@
  *      v_cache         bf16 [num_blocks][Hkv][bs/8][D][8]
  *                      (V transposed inside a block in chunks of 8 slots:
  *                       slot s, dim d at [s/8][d][s%8])
+ *                      This pool layout is part of the contract: a caller
+ *                      states it in sa_dims.cache_layout (SA_LAYOUT_K2_V8).
+ *                      Pools of plain rows, [num_blocks][Hkv][bs][D] for K
+ *                      and V (SA_LAYOUT_PLAIN, also what a zero-filled
+ *                      sa_dims says), are refused with SA_ERR_UNSUPPORTED
+ *                      rather than read wrongly.
  *      block_table     int32 [B][max_blocks_per_seq]
  *      seq_lens        int32 [B]
  *      sinks           fp32 [Hq] (may be NULL: no sink)
@@ -97,7 +103,20 @@ typedef struct sa_dims {
                                     Needs window <= 0 and T*(Hq/Hkv) <= 16
                                     (SA_ERR_UNSUPPORTED otherwise); not with
                                     RoPE or SA_VARIANT_VALU.                   */
+    int32_t cache_layout;        /* layout of k_cache / v_cache: must be
+                                    SA_LAYOUT_K2_V8 for every call that takes
+                                    the pools or sizes a call on them
+                                    (SA_ERR_UNSUPPORTED otherwise; sa_combine
+                                    ignores it)                                */
 } sa_dims;
+
+/* Pool layouts (sa_dims.cache_layout). */
+enum {
+    SA_LAYOUT_PLAIN = 0,   /* K and V [num_blocks][Hkv][bs][D]: not supported   */
+    SA_LAYOUT_K2_V8 = 1    /* K [num_blocks][Hkv][2][bs][D/2] (two slot-major
+                              halves), V [num_blocks][Hkv][bs/8][D][8] (chunks
+                              of 8 slots): the layout the kernels read         */
+};
 
 enum {
     SA_OK = 0,
@@ -248,13 +267,22 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
                        const sa_dims* dims, void* stream);
 
 /*
- * Log-sum-exp combine of num_splits partials per (b, h) with the sink:
+ * Log-sum-exp combine of split-K partials with the sink (the tutorial setup
+ * page, file table, FlashAttention chapter (S12): the tiled online softmax
+ * whose per-tile (o, lse) pairs merge this way; SimpleLLM README,
+ * optimisation table, fused decode-attention row: the attention sink, which
+ * joins the normaliser once and has no value row).  For num_splits partials
+ * per (b, h):
  *     M = max(max_j part_lse[b][h][j], sigma_h)
  *     out[b][h] = sum_j e^(lse_j - M) part_o[b][h][j] / (sum_j e^(lse_j - M) + e^(sigma_h - M))
  * rounded to bf16; partials with lse = -inf carry no weight (whatever their
  * part_o holds, NaN included, never reaches out; the whole [B][Hq][S][D]
- * part_o must still be allocated); 0 where nothing remains.  Uses num_seqs,
- * num_q_heads and head_dim of dims.
+ * part_o must still be allocated); 0 where nothing remains.  This equals
+ * the one-shot attention of sa_decode_attention when the partials cover the
+ * attended positions in disjoint sets.  Uses num_seqs, num_q_heads,
+ * head_dim and num_query_tokens of dims (rows (b*T + t)*Hq + h).  Errors:
+ * SA_ERR_INVALID_ARG (NULL dims, part_o, part_lse or out with num_seqs > 0;
+ * num_splits < 1; negative sizes), SA_ERR_UNSUPPORTED (head_dim != 64).
  */
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
                int32_t num_splits, sa_bf16* out, const sa_dims* dims, void* stream);

@@ -28,6 +28,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK = 0
+LAYOUT_PLAIN = 0        # K and V [NB][Hkv][bs][D]: refused by the library
+LAYOUT_K2_V8 = 1        # the pools this binding describes (see the module docstring)
 VARIANT_DEFAULT = 0
 VARIANT_MFMA_TWO_PASS = 1
 VARIANT_MFMA_FUSED = 2
@@ -47,6 +49,7 @@ class Dims(ctypes.Structure):
         ("num_splits", ctypes.c_int32),
         ("variant", ctypes.c_int32),
         ("num_query_tokens", ctypes.c_int32),
+        ("cache_layout", ctypes.c_int32),
     ]
 
 
@@ -174,7 +177,8 @@ def _cache_dims(k_cache, v_cache, block_table, B, num_splits, variant):
                          f"got {tuple(v_cache.shape)}")
     if block_table.shape[0] != B:
         raise ValueError("block_table must have one row per sequence")
-    return Dims(B, 0, Hkv, D, bs, block_table.shape[1], NB, int(num_splits), int(variant), 0)
+    return Dims(B, 0, Hkv, D, bs, block_table.shape[1], NB, int(num_splits), int(variant), 0,
+                LAYOUT_K2_V8)
 
 
 def dims_for(q, k_cache, v_cache, block_table, num_splits=0, variant=VARIANT_DEFAULT) -> Dims:
@@ -412,7 +416,7 @@ def combine(part_o, part_lse, sinks=None, out=None, stream=None):
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
     _check(out, "out", torch.bfloat16, 3, dev)
-    d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0, 0)
+    d = Dims(B, Hq, 1, D, 16, 1, 1, 0, 0, 0, LAYOUT_K2_V8)
     with _on(dev):
         st = load().sa_combine(_ptr(part_o), _ptr(part_lse), _ptr(sinks), int(S), _ptr(out),
                                ctypes.byref(d), _stream(stream, dev))

@@ -34,6 +34,9 @@ int check_dims(const sa_dims* d, int32_t window) {
         d->head_dim < 1 || d->block_size < 1 || d->num_query_tokens < 0)
         return SA_ERR_INVALID_ARG;
     if (d->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
+    // the kernels read only the split-K / chunked-V pools; plain-row pools
+    // (or a caller that never set the field) would be read as garbage
+    if (d->cache_layout != SA_LAYOUT_K2_V8) return SA_ERR_UNSUPPORTED;
     if (d->num_q_heads % d->num_kv_heads) return SA_ERR_UNSUPPORTED;
     // (query tokens) x (heads per KV head) columns fill one 16-column MFMA tile
     if ((long long)query_tokens(d) * (d->num_q_heads / d->num_kv_heads) > sa::kMaxGroup)

@@ -33,7 +33,8 @@ def lib():
 
 def good_dims(**kw):
     d = dict(num_seqs=2, num_q_heads=16, num_kv_heads=2, head_dim=64, block_size=16,
-             max_blocks_per_seq=8, num_blocks=32, num_splits=0, variant=0)
+             max_blocks_per_seq=8, num_blocks=32, num_splits=0, variant=0,
+             cache_layout=sa.LAYOUT_K2_V8)
     d.update(kw)
     return sa.Dims(**d)
 
@@ -69,6 +70,9 @@ def test_status_strings(lib):
     (dict(num_query_tokens=-1), SA_ERR_INVALID_ARG),
     (dict(num_query_tokens=3), SA_ERR_UNSUPPORTED),               # 3 tokens x G 8 > 16
     (dict(max_blocks_per_seq=1 << 27), SA_ERR_UNSUPPORTED),       # capacity 2^31 tokens
+    (dict(cache_layout=sa.LAYOUT_PLAIN), SA_ERR_UNSUPPORTED),     # [NB][Hkv][bs][D] pools
+    (dict(cache_layout=2), SA_ERR_UNSUPPORTED),                   # no such layout
+    (dict(cache_layout=-1), SA_ERR_UNSUPPORTED),
 ])
 def test_bad_dims_rejected_everywhere(lib, kw, status):
     d = good_dims(**kw)
@@ -279,3 +283,33 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
     assert ws(8, 512, 8) == static(8, 8)                 # 512
     assert ws(128, 128, 2) == balanced(128)              # 2048
     assert ws(4, 512, 8) == balanced(4)                  # 256
+
+
+def test_plain_row_pools_are_refused_not_misread(lib):
+    """A caller describing pools of plain rows ([NB][Hkv][bs][D] for K and V),
+    or one that left sa_dims zero-filled past the shapes, gets
+    SA_ERR_UNSUPPORTED from every call that takes the pools, before any
+    launch; sa_combine, which takes no pool, does not look at the field."""
+    for layout in (sa.LAYOUT_PLAIN, 0):
+        d = good_dims(cache_layout=layout)
+        assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == SA_ERR_UNSUPPORTED
+        assert lib.sa_decode_workspace_bytes(ctypes.byref(d), 0) == 0
+        assert lib.sa_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, ctypes.byref(d),
+                                None) == SA_ERR_UNSUPPORTED
+        for W in (0, 64):
+            assert lib.sa_decode_attention(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, W, FAKE,
+                                           ctypes.byref(d), FAKE, 1 << 30, None) \
+                == SA_ERR_UNSUPPORTED
+            assert lib.sa_decode_attention_append(*([FAKE] * 8), W, FAKE, ctypes.byref(d),
+                                                  FAKE, 1 << 30, None) == SA_ERR_UNSUPPORTED
+        assert lib.sa_decode_partials(FAKE, FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE,
+                                      ctypes.byref(d), None) == SA_ERR_UNSUPPORTED
+        r = sa.Rope(0x10000, 0x10000, 16, sa.ROPE_HALF)
+        assert lib.sa_decode_attention_append_rope(*([FAKE] * 8), 0, ctypes.byref(r), FAKE,
+                                                   ctypes.byref(d), FAKE, 1 << 30, None) \
+            == SA_ERR_UNSUPPORTED
+    assert sa.Dims().cache_layout == sa.LAYOUT_PLAIN     # what a zero-filled struct says
+    # the combine's own checks still run first (here: no splits)
+    d = good_dims(cache_layout=sa.LAYOUT_PLAIN)
+    assert lib.sa_combine(FAKE, FAKE, None, 0, FAKE, ctypes.byref(d), None) == SA_ERR_INVALID_ARG
+
