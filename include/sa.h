@@ -16,7 +16,9 @@
  *  - Every pointer is DEVICE memory owned by the caller, except the
  *    `const sa_dims*`, which is host memory read during the call only.
  *    The library never allocates, frees or synchronises; it keeps no
- *    global mutable state and is safe to call from several host threads.
+ *    global mutable state (save the per-device address of the no-allocation
+ *    call's scratch, set once under a lock) and is safe to call from several
+ *    host threads.
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL is the
  *    null stream of the calling thread's current HIP device).  A return of
  *    SA_OK means the work was enqueued; a fault inside a kernel surfaces as a
@@ -124,7 +126,9 @@ enum {
     SA_ERR_UNSUPPORTED = -2,    /* D != 64, Hq % Hkv != 0, Hq/Hkv > 16, bs,
                                    capacity > 2^30 tokens, ...                  */
     SA_ERR_WORKSPACE = -3,      /* workspace missing or too small               */
-    SA_ERR_HIP = -4             /* the HIP runtime refused a launch             */
+    SA_ERR_HIP = -4,            /* the HIP runtime refused a launch             */
+    SA_ERR_SCRATCH = -5         /* the no-allocation call needs more than the
+                                   library's SA_SCRATCH_BYTES of scratch        */
 };
 
 /* Kernel variants (sa_dims.variant).  All give results within the same
@@ -214,6 +218,31 @@ int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_
                                const float* sinks, int32_t window, sa_bf16* out,
                                const sa_dims* dims, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Exactly
+ * sa_decode_attention_append without a workspace argument, with
+ * bit-identical results.  What the call would keep in a workspace (split-K
+ * partials, the balanced kernel's unit records, completion counters) goes to
+ * a device array the library owns: SA_SCRATCH_BYTES bytes on each GPU,
+ * created zero-filled with the library's code on that device and held until
+ * the process ends.  The call allocates and frees nothing; on its first call
+ * on a device it looks the array's address up (hipGetSymbolAddress) with
+ * that device current and keeps it (under a lock: the only state the library
+ * keeps).  A call whose sa_decode_workspace_bytes exceeds SA_SCRATCH_BYTES
+ * returns SA_ERR_SCRATCH before launching anything.  Every call on one GPU
+ * uses that GPU's one array and leaves its counters at zero, as it found
+ * them; the rest is rewritten by each call before it is read.  Calls that
+ * may overlap on one GPU (several streams, several host threads) race on the
+ * array and must be serialised by the caller.
+ */
+#define SA_SCRATCH_BYTES ((size_t)32 << 20)
+int sa_decode_attention_append_noalloc(const sa_bf16* q, const sa_bf16* k_new,
+                                       const sa_bf16* v_new, sa_bf16* k_cache, sa_bf16* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const float* sinks, int32_t window, sa_bf16* out,
+                                       const sa_dims* dims, void* stream);
 
 /*
  * Rotary position embedding of the new token (SimpleLLM README, optimisation

@@ -28,6 +28,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK = 0
+SA_ERR_SCRATCH = -5
+SCRATCH_BYTES = 32 << 20      # the library's per-GPU scratch (SA_SCRATCH_BYTES)
 LAYOUT_PLAIN = 0        # K and V [NB][Hkv][bs][D]: refused by the library
 LAYOUT_K2_V8 = 1        # the pools this binding describes (see the module docstring)
 VARIANT_DEFAULT = 0
@@ -75,7 +77,8 @@ class SAError(RuntimeError):
 _lib = None
 EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
            "sa_decode_attention", "sa_decode_attention_append",
-           "sa_decode_attention_append_rope", "sa_decode_partials",
+           "sa_decode_attention_append_noalloc", "sa_decode_attention_append_rope",
+           "sa_decode_partials",
            "sa_combine", "sa_read_bandwidth_probe", "sa_status_string")
 
 
@@ -102,6 +105,9 @@ def load(path: Optional[str] = None):
     lib.sa_decode_attention_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, vp, dp, vp,
                                                sz, vp]
     lib.sa_decode_attention_append.restype = ctypes.c_int
+    lib.sa_decode_attention_append_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                                       vp, dp, vp]
+    lib.sa_decode_attention_append_noalloc.restype = ctypes.c_int
     lib.sa_decode_attention_append_rope.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                                     ctypes.POINTER(Rope), vp, dp, vp, sz, vp]
     lib.sa_decode_attention_append_rope.restype = ctypes.c_int
@@ -322,6 +328,33 @@ def decode_attention_append(q, k_new, v_new, k_cache, v_cache, block_table, seq_
             _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d), _ptr(workspace),
             ws_bytes, _stream(stream, dev))
     _raise(st, "sa_decode_attention_append")
+    return out
+
+
+def decode_attention_append_noalloc(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens,
+                                    out, sinks=None, window=0, num_splits=0,
+                                    variant=VARIANT_DEFAULT, stream=None):
+    """The fused decode step without a workspace: its partials live in the
+    library's own per-GPU scratch array, so neither the library nor this
+    binding allocates (``out`` is required).  Calls that may overlap on one
+    GPU race on that array.  Returns ``out``."""
+    d = dims_for(q, k_cache, v_cache, block_table, num_splits, variant)
+    dev = q.device
+    _check(seq_lens, "seq_lens", torch.int32, 1, dev)
+    _check_new_rows(k_new, v_new, d, dev)
+    if sinks is not None:
+        _check(sinks, "sinks", torch.float32, 1, dev)
+        if sinks.shape[0] != d.num_q_heads:
+            raise ValueError("sinks must have one entry per query head")
+    _check(out, "out", torch.bfloat16, q.dim(), dev)
+    if out.shape != q.shape:
+        raise ValueError("out must have the shape of q")
+    with _on(dev):
+        st = load().sa_decode_attention_append_noalloc(
+            _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+            _ptr(seq_lens), _ptr(sinks), int(window), _ptr(out), ctypes.byref(d),
+            _stream(stream, dev))
+    _raise(st, "sa_decode_attention_append_noalloc")
     return out
 
 

@@ -11,6 +11,8 @@
 #include "plan.h"
 #include "sa_internal.h"
 
+static_assert(SA_SCRATCH_BYTES == sa::kScratchBytes, "the header states the scratch size");
+
 namespace {
 
 using sa::kHeadDim;
@@ -127,12 +129,15 @@ size_t sa_decode_workspace_bytes(const sa_dims* dims, int32_t window) {
 
 namespace {
 
-// Attention, and with k_new/v_new the KV append in the same launch.
+// Attention, and with k_new/v_new the KV append in the same launch.  With
+// lib_scratch the call takes its workspace from the library's own device
+// array instead of `workspace` (which is then ignored): after every argument
+// check, so a bad call still touches no HIP state.
 int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
            const sa_bf16* k_cache, const sa_bf16* v_cache, const int32_t* block_table,
            const int32_t* seq_lens, const float* sinks, int32_t window, const sa_rope* rope,
            sa_bf16* out, const sa_dims* dims, void* workspace, size_t workspace_bytes,
-           void* stream) {
+           void* stream, bool lib_scratch = false) {
     int st = check_dims(dims, window);
     if (st != SA_OK) return st;
     if (dims->num_seqs == 0) return SA_OK;
@@ -157,6 +162,15 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
                     : sa::launch_decode_mfma(args, with_rope, strm);
     };
     const WorkspaceLayout wl = workspace_layout(dims, window, p, mode);
+    if (lib_scratch) {
+        if (wl.total > sa::kScratchBytes) return SA_ERR_SCRATCH;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (wl.total) {
+            if (sa::scratch_pointer(&workspace) != hipSuccess) return SA_ERR_HIP;
+            workspace_bytes = sa::kScratchBytes;
+        }
+    }
     if (wl.total && (!workspace || workspace_bytes < wl.total)) return SA_ERR_WORKSPACE;
 
     sa::DecodeArgs a = decode_args(dims, window, p);
@@ -240,6 +254,19 @@ int sa_decode_attention_append(const sa_bf16* q, const sa_bf16* k_new, const sa_
                   nullptr, out, dims, workspace, workspace_bytes, stream);
 }
 
+int sa_decode_attention_append_noalloc(const sa_bf16* q, const sa_bf16* k_new,
+                                       const sa_bf16* v_new, sa_bf16* k_cache, sa_bf16* v_cache,
+                                       const int32_t* block_table, const int32_t* seq_lens,
+                                       const float* sinks, int32_t window, sa_bf16* out,
+                                       const sa_dims* dims, void* stream) {
+    const int st = check_dims(dims, window);
+    if (st != SA_OK) return st;
+    if (dims->num_seqs == 0) return SA_OK;
+    if (!k_new || !v_new) return SA_ERR_INVALID_ARG;
+    return decode(q, k_new, v_new, k_cache, v_cache, block_table, seq_lens, sinks, window,
+                  nullptr, out, dims, nullptr, 0, stream, /*lib_scratch=*/true);
+}
+
 int sa_decode_attention_append_rope(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
                                     sa_bf16* k_cache, sa_bf16* v_cache,
                                     const int32_t* block_table, const int32_t* seq_lens,
@@ -313,6 +340,9 @@ const char* sa_status_string(int status) {
         case SA_ERR_UNSUPPORTED: return "unsupported shape";
         case SA_ERR_WORKSPACE: return "workspace missing or too small";
         case SA_ERR_HIP: return "HIP launch failed";
+        case SA_ERR_SCRATCH:
+            return "call needs more device scratch than the library's fixed array "
+                   "(SA_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

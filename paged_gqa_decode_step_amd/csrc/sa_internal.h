@@ -86,6 +86,13 @@ struct CombineArgs {
     int32_t B, Hq, num_splits;
 };
 
+// Bytes of the library-owned device scratch (one array per GPU) that the
+// no-allocation entry point uses instead of a caller's workspace.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+// Device address of that array on the calling thread's current device (looked
+// up with hipGetSymbolAddress on the first call on a device, then kept).
+hipError_t scratch_pointer(void** out);
+
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // rope: the kernels built with the rotary embedding of q and k_new; a.T > 1:
 // the kernels built for several causal query tokens per sequence

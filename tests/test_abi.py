@@ -41,7 +41,7 @@ def good_dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
     assert set(names) == set(sa.EXPORTS)
@@ -313,3 +313,29 @@ def test_plain_row_pools_are_refused_not_misread(lib):
     d = good_dims(cache_layout=sa.LAYOUT_PLAIN)
     assert lib.sa_combine(FAKE, FAKE, None, 0, FAKE, ctypes.byref(d), None) == SA_ERR_INVALID_ARG
 
+
+
+def test_noalloc_call_validates_before_touching_the_device(lib):
+    """The no-allocation step checks its arguments, and that the call fits the
+    library's scratch, before any HIP call (so these run without a GPU)."""
+    d = good_dims()
+    for i in range(8):                    # q, k_new, v_new, pools, table, lengths, (sinks)
+        if i == 7:
+            continue                      # sinks may be NULL
+        args = [FAKE] * 8
+        args[i] = None
+        assert lib.sa_decode_attention_append_noalloc(*args, 0, FAKE, ctypes.byref(d),
+                                                      None) == SA_ERR_INVALID_ARG
+    assert lib.sa_decode_attention_append_noalloc(*([FAKE] * 8), 0, None, ctypes.byref(d),
+                                                  None) == SA_ERR_INVALID_ARG
+    d = good_dims(cache_layout=sa.LAYOUT_PLAIN)
+    assert lib.sa_decode_attention_append_noalloc(*([FAKE] * 8), 0, FAKE, ctypes.byref(d),
+                                                  None) == SA_ERR_UNSUPPORTED
+    # a static split of 4096 x 64 heads x 8 partitions needs 512 MiB of partials
+    big = good_dims(num_seqs=4096, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=512,
+                    num_blocks=1 << 20, variant=1)
+    need = lib.sa_decode_workspace_bytes(ctypes.byref(big), 0)
+    assert need > sa.SCRATCH_BYTES
+    assert lib.sa_decode_attention_append_noalloc(*([FAKE] * 8), 0, FAKE, ctypes.byref(big),
+                                                  None) == sa.SA_ERR_SCRATCH
+    assert "scratch" in sa.status_string(sa.SA_ERR_SCRATCH)
