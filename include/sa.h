@@ -138,8 +138,12 @@ enum {
     SA_VARIANT_MFMA_TWO_PASS = 1, /* MFMA partitions, separate combine launch  */
     SA_VARIANT_MFMA_FUSED = 2,    /* MFMA partitions, combine by the last one  */
     SA_VARIANT_VALU = 3,          /* vector-ALU partitions (no MFMA)           */
-    SA_VARIANT_MFMA_BALANCED = 4  /* MFMA, equal work per wavefront across the
+    SA_VARIANT_MFMA_BALANCED = 4, /* MFMA, equal work per wavefront across the
                                      batch, merge launch for split units       */
+    SA_VARIANT_MFMA_BALANCED_LAST_MERGES = 5 /* the same split; the last
+                                     wavefront to finish a split unit merges it
+                                     (agent-coherent stores and a device-scope
+                                     counter instead of the merge launch)      */
 };
 
 /*
@@ -168,8 +172,8 @@ int32_t sa_decode_num_splits(const sa_dims* dims, int32_t window);
 
 /*
  * Device workspace bytes sa_decode_attention needs for these dims and window
- * (0 when it needs none, also returned for invalid dims).  The first 256 KiB
- * of a workspace hold completion counters: zero-fill the workspace once
+ * (0 when it needs none, also returned for invalid dims).  The first 1 MiB
+ * of a workspace holds completion counters: zero-fill the workspace once
  * before its first use; every call leaves those counters at zero again, so
  * one workspace of the largest size needed serves any sequence of calls on a
  * stream, whatever their dims.  Calls that may run at the same time need

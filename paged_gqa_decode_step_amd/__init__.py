@@ -37,6 +37,7 @@ VARIANT_MFMA_TWO_PASS = 1
 VARIANT_MFMA_FUSED = 2
 VARIANT_VALU = 3
 VARIANT_MFMA_BALANCED = 4
+VARIANT_MFMA_BALANCED_LAST_MERGES = 5
 
 
 class Dims(ctypes.Structure):

@@ -16,10 +16,24 @@
 // names the online softmax it rests on).
 //
 // Every wavefront derives T and the unit layout itself from seq_lens (an
-// inclusive scan in LDS), so there is no planning launch.  The wavefronts
-// holding a unit's first and last steps record, for the combine kernel, the
-// unit's first partial slot and its last wavefront.  The per-step MFMA
-// machinery is mfma_attend.h.
+// inclusive scan in LDS), so there is no planning launch.
+//
+// Merging a unit spread over wavefronts i0..i1.  By default the wavefronts
+// holding a unit's first and last steps record the unit's first partial
+// slot and its last wavefront, and combine_stream_kernel merges in a launch
+// of its own.  With FUSED (SA_VARIANT_MFMA_BALANCED_LAST_MERGES) each of them
+// stores its segment (o, lse) with agent-coherent stores (sc1: written
+// through this XCD's L2, so a wavefront on another XCD reads them) as soon as
+// it has it, and once its whole range is done waits until those stores are
+// complete and counts its arrivals on the units' counters with device-scope
+// atomics; the wavefront that arrives last at a unit reads every segment
+// with agent-coherent loads, merges them with the sink, writes the bf16
+// output and returns the counter to zero.  That needs no device-scope fence
+// (an L2 write-back) and no second launch, but measured slower than the
+// merge launch on every workload (the write-back wait, the counted arrival
+// and the merging wavefront's reads are dependent round trips, and a unit
+// spread over many wavefronts is merged by one), so it is not the default.
+// The per-step MFMA machinery is mfma_attend.h.
 #include "mfma_attend.h"
 
 namespace sa {
@@ -37,11 +51,106 @@ __device__ __forceinline__ long long wave_start(long long i, long long T, long l
     return i * T / NW;
 }
 
-// Sequence b has nothing to attend: zero outputs, and for each of its units a
-// record (first slot in wavefront i, last wavefront i) that the combine
-// kernel reads as "done".
+// wavefront holding step x: the i with wave_start(i) <= x < wave_start(i+1)
+__device__ __forceinline__ int wave_of(long long x, long long T, long long NW) {
+    return (int)(((x + 1) * NW - 1) / T);
+}
+
+// A segment of a unit in the fused merge: o = acc / l (16 values a lane) and
+// the log2-domain lse of the lane's column, stored lane-major so each store
+// and load instruction covers 256 contiguous bytes.
+constexpr int kSegFloats = 17 * 64;
+
+__device__ __forceinline__ void store_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_segment(float* seg, int lane, const State& st, float l_tot) {
+    // a column with no slot in the segment (several query tokens only) has
+    // weight 0: lse = -inf, o = 0
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.0f / l_tot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) store_agent(seg + (j * 4 + e) * 64 + lane, st.acc[j][e] * inv);
+    store_agent(seg + 16 * 64 + lane, empty ? -INFINITY : st.m + __builtin_amdgcn_logf(l_tot));
+}
+
+// The last wavefront to arrive at a unit spread over wavefronts i0..i1 merges
+// their segments (its own included, read back like the others) with the sink
+// and writes the bf16 output.  Segment k is wavefront i0 + k's: in slot
+// `first` for k = 0 (the unit may be that wavefront's second), else in slot
+// 2 (i0 + k) (its first).
+constexpr int kMergeChunk = 4;
+__device__ __forceinline__ void merge_unit(const DecodeArgs& a, int b, int g, int lane, int i0,
+                                           int i1, int first) {
+    // running merge, log2 domain: out = num / (den + 2^(sigma - M)), all
+    // scaled by 2^-M
+    float M = -INFINITY;
+    float num[16];
+    float den = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) num[v] = 0.f;
+    const int nseg = i1 - i0 + 1;
+    for (int k0 = 0; k0 < nseg; k0 += kMergeChunk) {
+        float lse[kMergeChunk], o[kMergeChunk][16];
+#pragma unroll
+        for (int c = 0; c < kMergeChunk; ++c) {
+            const int k = k0 + c;               // wave-uniform
+            lse[c] = -INFINITY;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[c][v] = 0.f;
+            if (k < nseg) {
+                const float* seg =
+                    a.part_o + (size_t)(k == 0 ? first : 2 * (i0 + k)) * kSegFloats;
+                lse[c] = load_agent(seg + 16 * 64 + lane);
+#pragma unroll
+                for (int v = 0; v < 16; ++v) o[c][v] = load_agent(seg + v * 64 + lane);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kMergeChunk; ++c) {
+            if (lse[c] == -INFINITY) continue;  // not a segment, or an empty column
+            const float M2 = fmaxf(M, lse[c]);
+            const float r = __builtin_amdgcn_exp2f(M - M2);       // 0 while M = -inf
+            const float w = __builtin_amdgcn_exp2f(lse[c] - M2);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) num[v] = num[v] * r + w * o[c][v];
+            den = den * r + w;
+            M = M2;
+        }
+    }
+    const Col c = column(a, lane);
+    if (!c.ok) return;
+    // the sink joins the denominator only
+    const float sig = a.sinks ? a.sinks[g * a.G + c.h] * kLog2e : -INFINITY;
+    const float M2 = fmaxf(M, sig);
+    uint16_t* op = a.out + col_row(a, b, g, c) * kHeadDim + 4 * (lane >> 4);
+    if (M2 == -INFINITY) {                      // nothing attended and no sink
+        write_zero(a, b, g, lane);
+        return;
+    }
+    const float r = __builtin_amdgcn_exp2f(M - M2);
+    const float inv = 1.0f / (den * r + __builtin_amdgcn_exp2f(sig - M2));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const u32x2_t ov = {pack_bf16(num[j * 4] * r * inv, num[j * 4 + 1] * r * inv),
+                            pack_bf16(num[j * 4 + 2] * r * inv, num[j * 4 + 3] * r * inv)};
+        *reinterpret_cast<u32x2_t*>(op + 16 * j) = ov;
+    }
+}
+
+// Sequence b has nothing to attend: zero outputs, and (without FUSED) for
+// each of its units a record (first slot in wavefront i, last wavefront i)
+// that the combine kernel reads as "done".
+template <bool FUSED>
 __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, int lane) {
     for (int g = 0; g < a.Hkv; ++g) write_zero(a, b, g, lane);
+    if (FUSED) return;
     // one record per KV head, however many heads there are (the workspace is
     // reused from call to call, so a record left out would be a stale one)
     for (int g = lane; g < a.Hkv; g += 64) {
@@ -56,7 +165,7 @@ __device__ __forceinline__ void finish_empty(const DecodeArgs& a, int b, int i, 
 #define SA_STREAM_OCC 0
 #endif
 
-template <int BSL, bool ROPE, bool MULTI>
+template <int BSL, bool ROPE, bool MULTI, bool FUSED>
 __global__ __launch_bounds__(64)
 #if SA_STREAM_OCC > 0
 __attribute__((amdgpu_waves_per_eu(SA_STREAM_OCC, SA_STREAM_OCC)))
@@ -92,14 +201,14 @@ void decode_stream_kernel(const DecodeArgs a) {
     const long long T = carry;
     if (T == 0) {
         // nothing attended anywhere: every output is 0
-        for (int bz = i; bz < a.B; bz += NW) finish_empty(a, bz, i, lane);
+        for (int bz = i; bz < a.B; bz += NW) finish_empty<FUSED>(a, bz, i, lane);
         return;
     }
     // the host launches this kernel only when sequences x KV heads x the
     // table's capacity in steps stays below 2^31, so the walk runs on 32-bit
     // wave-uniform values
     if (i == 0)                   // sequences before the first with a step
-        for (int bz = 0; bz < a.B && s_end[bz] == 0; ++bz) finish_empty(a, bz, 0, lane);
+        for (int bz = 0; bz < a.B && s_end[bz] == 0; ++bz) finish_empty<FUSED>(a, bz, 0, lane);
     // The launch sizes NW from the table's capacity; with fewer steps than
     // that, only the first T wavefronts take part, so that every wavefront
     // in use holds at least one step and the wavefronts a unit spans are
@@ -120,6 +229,9 @@ void decode_stream_kernel(const DecodeArgs a) {
         b = __builtin_amdgcn_readfirstlane(lo);
     }
     int slot = 0;                 // 0: first unit of this wavefront, 1: last
+    // (FUSED) segments stored in slot 0 / 1, whose arrivals are still to count
+    int pend_b[2] = {0, 0}, pend_g[2] = {0, 0}, pend_start[2] = {0, 0}, pend_steps[2] = {1, 1};
+    bool pend_on[2] = {false, false};
     while (x < x1) {
         const int L = __builtin_amdgcn_readfirstlane(s_len[b]);
         const int n = attended(a, L);
@@ -141,13 +253,23 @@ void decode_stream_kernel(const DecodeArgs a) {
         attend<BSL, ROPE, MULTI, 3>(a, u, s0 * kStepTokens, min(n, s1 * kStepTokens), qop0, qop1,
                                     st);
         const float l_tot = st.total();
-        if (lane == 0) {
+        if (!FUSED && lane == 0) {
             int* seg = a.unit_seg + 2 * (b * a.Hkv + g);
             if (s0 == 0) seg[0] = 2 * i + slot;    // this wavefront's slot for the unit
             if (s1 == steps) seg[1] = i;
         }
         if (s0 == 0 && s1 == steps) {
             write_out(a, b, g, lane, st, l_tot);
+        } else if (FUSED) {
+            // a segment of a unit other wavefronts share: stored now, its
+            // arrival counted once this wavefront's range is done (so the
+            // stream never waits for the stores)
+            store_segment(a.part_o + (size_t)(2 * i + slot) * kSegFloats, lane, st, l_tot);
+            pend_b[slot] = b;
+            pend_g[slot] = g;
+            pend_start[slot] = ustart;
+            pend_steps[slot] = steps;
+            pend_on[slot] = true;
         } else {
             // partial slot: T*G rows, one per (query token, head) column
             const int ncol = a.T * a.G;
@@ -160,10 +282,38 @@ void decode_stream_kernel(const DecodeArgs a) {
         if (x >= end_b) {         // next sequence that has any step
             ++b;
             while (b < a.B && __builtin_amdgcn_readfirstlane(attended(a, s_len[b])) == 0) {
-                finish_empty(a, b, i, lane);
+                finish_empty<FUSED>(a, b, i, lane);
                 ++b;
             }
         }
+    }
+    if (!FUSED || !(pend_on[0] || pend_on[1])) return;
+    // Count this wavefront's arrivals at the units it left segments of, once
+    // every store of those segments is complete (agent-visible: they are
+    // sc1); the wavefront that arrives last at a unit merges it.  Lanes 0 and
+    // 1 count the two segments at once.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int old = -1;
+    if (lane < 2 && pend_on[lane])
+        old = __hip_atomic_fetch_add(a.counters + pend_b[lane] * a.Hkv + pend_g[lane], 1,
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old0 = __builtin_amdgcn_readlane(old, 0);
+    const int old1 = __builtin_amdgcn_readlane(old, 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        if (!pend_on[p]) continue;
+        const int us = pend_start[p];
+        const int i0 = wave_of(us, T, NWe);
+        const int i1 = wave_of(us + pend_steps[p] - 1, T, NWe);
+        if ((p == 0 ? old0 : old1) != i1 - i0) continue;
+        // the last to arrive: every segment's stores completed before its
+        // arrival was counted.  The counter is this unit's alone until the
+        // next call, which finds it at zero again.
+        if (lane == 0)
+            __hip_atomic_store(a.counters + pend_b[p] * a.Hkv + pend_g[p], 0, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        const int first = 2 * i0 + (wave_start(i0, T, NWe) == us ? 0 : 1);
+        merge_unit(a, pend_b[p], pend_g[p], lane, i0, i1, first);
     }
 }
 
@@ -267,26 +417,33 @@ __global__ __launch_bounds__(64 * WAVES) void combine_stream_kernel(const Decode
     a.out[(size_t)bh * kHeadDim + lane] = __builtin_bit_cast(uint16_t, o);
 }
 
-template <bool ROPE, bool MULTI>
+template <bool ROPE, bool MULTI, bool FUSED>
 hipError_t launch_stream_partitions(const DecodeArgs& a, hipStream_t stream) {
     const size_t lds = (size_t)2 * a.B * sizeof(int);
     const dim3 grid(a.num_waves);
     switch (a.bs_log2) {
-        case 3: return launch(decode_stream_kernel<3, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
-        case 4: return launch(decode_stream_kernel<4, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
-        case 5: return launch(decode_stream_kernel<5, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
-        case 6: return launch(decode_stream_kernel<6, ROPE, MULTI>, grid, dim3(64), lds, stream, a);
+        case 3: return launch(decode_stream_kernel<3, ROPE, MULTI, FUSED>, grid, dim3(64), lds, stream, a);
+        case 4: return launch(decode_stream_kernel<4, ROPE, MULTI, FUSED>, grid, dim3(64), lds, stream, a);
+        case 5: return launch(decode_stream_kernel<5, ROPE, MULTI, FUSED>, grid, dim3(64), lds, stream, a);
+        case 6: return launch(decode_stream_kernel<6, ROPE, MULTI, FUSED>, grid, dim3(64), lds, stream, a);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <bool FUSED>
+hipError_t launch_stream_variant(const DecodeArgs& a, bool rope, hipStream_t stream) {
+    return a.T > 1 ? (rope ? hipErrorInvalidValue
+                           : launch_stream_partitions<false, true, FUSED>(a, stream))
+           : rope ? launch_stream_partitions<true, false, FUSED>(a, stream)
+                  : launch_stream_partitions<false, false, FUSED>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream) {
-    hipError_t e = a.T > 1 ? (rope ? hipErrorInvalidValue
-                                   : launch_stream_partitions<false, true>(a, stream))
-                 : rope ? launch_stream_partitions<true, false>(a, stream)
-                        : launch_stream_partitions<false, false>(a, stream);
+hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, bool fused_merge,
+                                hipStream_t stream) {
+    if (fused_merge) return launch_stream_variant<true>(a, rope, stream);
+    hipError_t e = launch_stream_variant<false>(a, rope, stream);
     if (e != hipSuccess) return e;
     // segments per unit if lengths were equal; picks the combine's width
     const long long units = (long long)a.B * a.Hkv;

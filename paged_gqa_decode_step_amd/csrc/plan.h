@@ -92,14 +92,22 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // fixed place, offset 0, in a region nothing else ever writes: every call
 // returns the counters it used to zero, so a workspace zeroed once stays
 // valid for any later call, whatever its dims or split count.
-constexpr int kCounterSlots = 1 << 16;   // (sequence, KV head) pairs a fused call may have
+constexpr int kCounterSlots = 1 << 18;   // (sequence, KV head) pairs a fused call may have
 constexpr size_t kCounterBytes = (size_t)kCounterSlots * sizeof(int32_t);
 
 struct WorkspaceLayout {
     size_t part_o, part_lse, counters, unit_seg, total;
 };
 
-enum class Mode { kStatic, kFused, kBalanced };
+// kBalanced: the balanced kernel and a merge launch; kBalancedLastMerges: the
+// balanced kernel, the last wavefront to finish a split unit merging it
+// (measured slower on every workload, so never the default: the counted
+// arrival and the agent-coherent reads cost more than the launch)
+enum class Mode { kStatic, kFused, kBalanced, kBalancedLastMerges };
+
+// floats of one segment slot of the balanced kernel's own merge (16 values
+// and an lse per lane)
+constexpr size_t kSegFloats = 17 * 64;
 
 // Upper bound on the balanced kernel's steps for these dims: every unit at
 // the table's capacity (the lengths live on the device).
@@ -125,11 +133,14 @@ long stream_waves(const sa_dims* d, int32_t window) {
 Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
     // the balanced kernel keeps its per-sequence table in LDS and walks steps
     // in 32-bit arithmetic
-    const bool fits_stream =
-        d->num_seqs <= kMaxStreamSeqs && stream_steps_upper(d, window) <= INT_MAX;
+    const bool fits_stream = d->num_seqs <= kMaxStreamSeqs &&
+                             stream_steps_upper(d, window) <= INT_MAX &&
+                             (long long)d->num_seqs * d->num_kv_heads <= kCounterSlots;
     switch (d->variant) {
         case SA_VARIANT_MFMA_BALANCED:
             return fits_stream ? Mode::kBalanced : Mode::kStatic;
+        case SA_VARIANT_MFMA_BALANCED_LAST_MERGES:
+            return fits_stream ? Mode::kBalancedLastMerges : Mode::kStatic;
         case SA_VARIANT_MFMA_FUSED:
             return (long long)d->num_seqs * d->num_kv_heads <= kCounterSlots ? Mode::kFused
                                                                              : Mode::kStatic;
@@ -159,6 +170,15 @@ Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
 WorkspaceLayout workspace_layout(const sa_dims* d, int32_t window, const Plan& p, Mode m) {
     WorkspaceLayout w{};
     size_t rows, lse;        // partial rows of D floats, and lse entries
+    if (m == Mode::kBalancedLastMerges) {
+        // two segment slots per wavefront, counters in front
+        w.counters = 0;
+        w.part_o = kCounterBytes;
+        w.total = w.part_o + align256((size_t)stream_waves(d, window) * 2 * kSegFloats *
+                                      sizeof(float));
+        w.part_lse = w.unit_seg = w.total;
+        return w;
+    }
     if (m == Mode::kBalanced) {
         const size_t slots = (size_t)stream_waves(d, window) * 2 * query_tokens(d) *
                              (d->num_q_heads / d->num_kv_heads);

@@ -46,7 +46,7 @@ int check_dims(const sa_dims* d, int32_t window) {
     if (query_tokens(d) > 1 && window > 0) return SA_ERR_UNSUPPORTED;   // a W-slot ring
     const int l = log2_exact(d->block_size);
     if (l < 3 || l > 6) return SA_ERR_UNSUPPORTED;
-    if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_MFMA_BALANCED)
+    if (d->variant < SA_VARIANT_DEFAULT || d->variant > SA_VARIANT_MFMA_BALANCED_LAST_MERGES)
         return SA_ERR_INVALID_ARG;
     if (window > 0 && (window + d->block_size - 1) / d->block_size > d->max_blocks_per_seq)
         return SA_ERR_INVALID_ARG;
@@ -195,12 +195,17 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     }
     hipStream_t s = (hipStream_t)stream;
     char* ws = (char*)workspace;
-    if (mode == Mode::kBalanced) {
+    if (mode == Mode::kBalanced || mode == Mode::kBalancedLastMerges) {
+        const bool fused = mode == Mode::kBalancedLastMerges;
         a.part_o = (float*)(ws + wl.part_o);
-        a.part_lse = (float*)(ws + wl.part_lse);
-        a.unit_seg = (int32_t*)(ws + wl.unit_seg);
+        if (fused) {
+            a.counters = (int32_t*)(ws + wl.counters);
+        } else {
+            a.part_lse = (float*)(ws + wl.part_lse);
+            a.unit_seg = (int32_t*)(ws + wl.unit_seg);
+        }
         a.num_waves = (int32_t)stream_waves(dims, window);
-        return to_status(sa::launch_decode_stream(a, with_rope, s));
+        return to_status(sa::launch_decode_stream(a, with_rope, fused, s));
     }
     if (p.splits == 1) {
         a.mode = sa::kWriteOut;

@@ -56,7 +56,8 @@ struct DecodeArgs {
     uint16_t* out;            // kWriteOut, kFusedCombine
     float* part_o;            // kWritePartials, kFusedCombine
     float* part_lse;
-    int32_t* counters;        // kFusedCombine: [B*Hkv], zero between calls
+    int32_t* counters;        // kFusedCombine, balanced kernel with its merge inside:
+                              // [B*Hkv] arrivals, zero between calls
     int32_t* unit_seg;        // balanced kernel: [B*Hkv][2] = (first partial slot, last
                               // wavefront) of each unit with a step, for its combine
     int32_t num_waves;        // balanced kernel: wavefronts in the grid
@@ -97,7 +98,11 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // rope: the kernels built with the rotary embedding of q and k_new; a.T > 1:
 // the kernels built for several causal query tokens per sequence
 hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream);
-hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, hipStream_t stream);
+// fused_merge: the last wavefront of a split unit merges it (part_o holds the
+// segments, counters the arrivals); otherwise a merge launch follows, reading
+// part_o / part_lse and the unit records in unit_seg
+hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, bool fused_merge,
+                                hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* data, size_t bytes, unsigned* sink, hipStream_t stream);

@@ -67,6 +67,7 @@ def test_status_strings(lib):
     (dict(num_blocks=0), SA_ERR_INVALID_ARG),
     (dict(num_splits=-2), SA_ERR_INVALID_ARG),
     (dict(variant=9), SA_ERR_INVALID_ARG),
+    (dict(variant=6), SA_ERR_INVALID_ARG),
     (dict(num_query_tokens=-1), SA_ERR_INVALID_ARG),
     (dict(num_query_tokens=3), SA_ERR_UNSUPPORTED),               # 3 tokens x G 8 > 16
     (dict(max_blocks_per_seq=1 << 27), SA_ERR_UNSUPPORTED),       # capacity 2^31 tokens
@@ -265,10 +266,11 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
     KV head) runs the static split (its workspace holds S partials for every
     output row); a smaller or larger grid, the balanced kernel (two partial
     slots per wavefront of 1024)."""
-    counters = (1 << 16) * 4
+    counters = (1 << 18) * 4
 
-    def ws(B, mbs, S):
-        d = good_dims(num_seqs=B, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=mbs)
+    def ws(B, mbs, S, variant=0):
+        d = good_dims(num_seqs=B, num_q_heads=64, num_kv_heads=8, max_blocks_per_seq=mbs,
+                      variant=variant)
         assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == S
         return lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
 
@@ -279,10 +281,15 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
     def balanced(B):
         rows = 1024 * 2 * 8                              # wavefronts x 2 slots x G
         return counters + rows * 64 * 4 + rows * 4 + B * 8 * 2 * 4
+
+    def balanced_last_merges(B):
+        return counters + 1024 * 2 * 17 * 64 * 4        # wavefronts x 2 segment slots
     assert ws(64, 128, 2) == static(64, 2)               # 1024 partitions
     assert ws(8, 512, 8) == static(8, 8)                 # 512
     assert ws(128, 128, 2) == balanced(128)              # 2048
     assert ws(4, 512, 8) == balanced(4)                  # 256
+    assert ws(128, 128, 2, variant=5) == balanced_last_merges(128)
+    assert ws(4, 512, 8, variant=4) == balanced(4)
 
 
 def test_plain_row_pools_are_refused_not_misread(lib):

@@ -15,7 +15,8 @@ from gpu_cases import assert_parity, bits, oracle_attention, out_f64, poison_tai
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = [0, 1, 2, 3, 4]  # default, static two-pass, static fused, vector-ALU, balanced
+VARIANTS = [0, 1, 2, 3, 4, 5]  # default, static two-pass, static fused, vector-ALU, balanced
+# (merge launch), balanced with the last wavefront of a unit merging it
 
 
 def attend(lib, layer, num_splits=0, variant=0, sinks="layer"):
@@ -265,7 +266,7 @@ def test_balanced_kernel_edge_cases(lib, W, B, lo, hi):
                              lens=lens, window=W, seed=2000 + B + W, device="cuda",
                              capacity=[max(1, L) for L in lens])
     ref = oracle_attention(layer)
-    for v in (0, 4):
+    for v in (0, 4, 5):
         a = attend(lib, layer, variant=v)
         assert_parity(out_f64(a), ref, f"balanced B={B} W={W} v={v}")
         assert torch.equal(a, attend(lib, layer, variant=v)), "not deterministic"
@@ -286,7 +287,7 @@ def test_empty_sequences_zeroed_over_stale_state(lib, lens):
     layer = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
                              lens=lens, capacity=cap, seed=1400 + B, device="cuda")
     ref = oracle_attention(layer)
-    for v in (0, 4):
+    for v in (0, 4, 5):
         lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
                              dirty.seq_lens, dirty.sinks, 0, workspace=ws, variant=v)
         out = torch.full_like(layer.q, float("nan"))
@@ -311,7 +312,7 @@ def test_empty_sequences_with_more_than_64_kv_heads(lib, lens):
                              lens=lens, capacity=[2048] * B, seed=1410 + sum(lens) // 7,
                              device="cuda")
     ref = oracle_attention(layer)
-    for v in (0, 4):
+    for v in (0, 4, 5):
         lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
                              dirty.seq_lens, dirty.sinks, 0, workspace=ws, variant=v)
         out = torch.full_like(layer.q, float("nan"))
@@ -341,7 +342,7 @@ def test_short_sequences_under_a_large_capacity(lib, W):
     layer = synth.make_layer(batch=B, q_heads=64, kv_heads=8, head_dim=64, block_size=16,
                              lens=lens, capacity=cap, window=W, seed=1700 + W, device="cuda")
     ref = oracle_attention(layer)
-    for v in (0, 4):
+    for v in (0, 4, 5):
         lib.decode_attention(dirty.q, dirty.k_cache, dirty.v_cache, dirty.block_table,
                              dirty.seq_lens, dirty.sinks, W, workspace=ws, variant=v)
         out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
@@ -406,7 +407,7 @@ def test_batch_at_the_balanced_limit(lib, B):
     layer = synth.make_layer(batch=B, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
                              lens=lens, seed=9200 + B, device="cuda")
     ref = oracle_attention(layer)
-    for v in (0, 4):
+    for v in (0, 4, 5):
         assert_parity(out_f64(attend(lib, layer, variant=v)), ref, f"B={B} variant={v}")
     s = sub_layer(layer, range(B))
     k_ref, v_ref = oracle.kv_append(s["k"], s["v"], s["k_new"], s["v_new"], s["bt"], s["lens"], 0)

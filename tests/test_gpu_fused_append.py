@@ -16,7 +16,8 @@ from gpu_cases import assert_parity, bits, oracle_attention, out_f64, sub_layer
 
 pytestmark = pytest.mark.gpu
 
-MFMA_VARIANTS = [0, 1, 2, 4]   # default, static two-pass, static fused combine, balanced
+MFMA_VARIANTS = [0, 1, 2, 4, 5]   # default, static two-pass, static fused combine,
+# balanced (merge launch), balanced with the last wavefront of a unit merging it
 
 
 def fresh_caches(layer):

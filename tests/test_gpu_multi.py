@@ -17,7 +17,7 @@ from gpu_cases import assert_parity, bits, out_f64, sub_layer
 
 pytestmark = pytest.mark.gpu
 
-MFMA_VARIANTS = [0, 1, 2, 4]
+MFMA_VARIANTS = [0, 1, 2, 4, 5]
 
 
 def tile_layer(lens, T, q_heads, kv_heads, seed, bs=16, capacity=None):

@@ -26,7 +26,7 @@ def draw(seed):
     lens = rng.integers(0, lmax + 1, size=B)
     lens[rng.random(B) < 0.1] = 0
     cap = lens + rng.integers(0, 3 * bs, size=B)
-    variant = int(rng.choice([0, 1, 2, 4]))
+    variant = int(rng.choice([0, 1, 2, 4, 5]))
     splits = int(rng.choice([0, 0, int(rng.integers(1, 20))]))
     return dict(hkv=hkv, G=G, bs=bs, B=B, window=window, lens=lens, cap=cap,
                 variant=variant, splits=splits)
@@ -73,7 +73,7 @@ def test_random_query_tile(lib, seed):
     bs = int(rng.choice([8, 16, 32, 64]))
     B = int(rng.integers(1, 25))
     lens = np.maximum(rng.integers(0, 2500, size=B), T)
-    variant = int(rng.choice([0, 1, 2, 4]))
+    variant = int(rng.choice([0, 1, 2, 4, 5]))
     splits = int(rng.choice([0, 0, int(rng.integers(1, 12))]))
     tag = f"seed {seed}: T={T} G={G} hkv={hkv} bs={bs} B={B} v={variant} S={splits}"
     layer, q, kn, vn = tm.tile_layer(lens.tolist(), T, hkv * G, hkv, seed=40_000 + seed, bs=bs)
@@ -105,7 +105,7 @@ def test_random_rope_step(lib, seed):
     window = int(rng.choice([0, 0, int(rng.integers(1, 200))]))
     lens = rng.integers(1, 2000, size=B)
     P = int(rng.choice([64, 4096]))            # rows of the angle tables
-    variant = int(rng.choice([0, 1, 2, 4]))
+    variant = int(rng.choice([0, 1, 2, 4, 5]))
     splits = int(rng.choice([0, 0, int(rng.integers(1, 12))]))
     tag = f"seed {seed}: {style} hkv={hkv} G={G} bs={bs} B={B} W={window} P={P} v={variant}"
     layer = synth.make_layer(batch=B, q_heads=hkv * G, kv_heads=hkv, head_dim=64, block_size=bs,

@@ -18,7 +18,7 @@ from gpu_cases import assert_parity, bits, out_f64, sub_layer
 pytestmark = pytest.mark.gpu
 
 STYLES = {"half": 0, "interleaved": 1}
-MFMA_VARIANTS = [0, 1, 2, 4]
+MFMA_VARIANTS = [0, 1, 2, 4, 5]
 
 
 def angle_tables(P, D=64, base=10000.0, device="cuda"):
@@ -112,7 +112,7 @@ def test_rope_positions_past_the_table(lib, style):
     layer = synth.make_layer(batch=3, q_heads=16, kv_heads=2, head_dim=64, block_size=16,
                              lens=lens, seed=7200, device="cuda")
     cos_t, sin_t = angle_tables(32)
-    check(lib, layer, cos_t, sin_t, style, splits=(0,), variants=[0, 4], what="table end")
+    check(lib, layer, cos_t, sin_t, style, splits=(0,), variants=[0, 4, 5], what="table end")
 
 
 def test_rope_ragged_batch64(lib):

@@ -38,7 +38,7 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("variant", [0, 2])
+@pytest.mark.parametrize("variant", [0, 2, 5])
 @pytest.mark.parametrize("case", sorted(CASES))
 def test_noalloc_equals_workspace_call(lib, case, variant):
     for i, kw in enumerate(CASES[case]):
