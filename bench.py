@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Benchmark of the decode step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch64_ragged]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch64_8k]
                     [--configs all|none] [--graph]
 
 A step is one pass of the whole hot path over one batch.  For the default
-workload it is the KV append and decode attention of a paged full-attention
-layer, then the KV append and decode attention of a sliding-window-128 ring
-layer.  The batch is 64 sequences with 64 query / 8 KV heads, D 64, block size
-16, and a ragged context of 512..8192 plus one appended token.  Inputs are
-seeded synthetic bf16 N(0,1) values, resident in HBM before timing starts.
+workload (batch64_8k, the metric's "batch 64, 8k ctx") it is one call that
+appends each sequence's new K/V row and attends over the paged cache: 64
+sequences of 8192 tokens (the new one included), 64 query / 8 KV heads, D 64,
+block size 16, a shuffled block table, learned sinks, split-K partitions and
+their merge.  ``--workload batch64_ragged`` times the two-layer step instead
+(a paged full layer and a sliding-window-128 ring layer, ragged contexts
+512..8192 plus the appended token).  Inputs are seeded synthetic bf16 N(0,1)
+values, resident in HBM before timing starts.
 
 Reported (one JSON line):
   value        the step's algorithmic bytes / its time (GB/s).  An attention
@@ -18,16 +21,19 @@ Reported (one JSON line):
                output rows); an append moves 4 KiB per sequence (read and write
                of K and V rows).
   roofline     the dominant call (the full-layer attention), timed with HIP
-               events on the stream it runs on, back to back.
-  The ring layer's pools (18 MB) would stay in the 256 MB Infinity Cache from
-  one step to the next; it rotates over enough input sets that every step reads
-  it from HBM, as a model with many layers would.
-  cpu_baseline the fp64 oracle on this host, on the same step.
+               events on the stream it runs on, back to back: the whole call,
+               and its decode kernel alone from the profiler's device trace.
+  cpu_baseline the fp64 oracle on this host's cores (a pool of worker
+               processes), on the same step.
+  batch64_ragged_step  the two-layer ragged step, timed the same way.  The
+               ring layer's pools (18 MB) would stay in the 256 MB Infinity
+               Cache from one step to the next; it rotates over enough input
+               sets that every step reads it from HBM, as a model with many
+               layers would.
   configs      every synthetic configuration: GPU us per call, GB/s and
-               fraction of peak, next to the oracle's seconds on a bounded
-               sample of the same inputs (scaled to the whole call).  Calls
-               whose inputs fit the 256 MB Infinity Cache rotate several input
-               sets so every call reads HBM.
+               fraction of peak, next to the oracle's seconds on the same
+               inputs.  Calls whose inputs fit the 256 MB Infinity Cache rotate
+               several input sets so every call reads HBM.
 """
 
 from __future__ import annotations
@@ -36,9 +42,11 @@ import argparse
 import contextlib
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
+import tempfile
 import time
 
 _ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -52,7 +60,11 @@ METRIC = "decode-attn µs/call + achieved HBM GB/s (% of peak), batch 64, 8k ctx
 # valid only for the exact sources it was taken on
 KERNEL_SRCS = [os.path.join(_ROOT, "paged_gqa_decode_step_amd", "csrc", f)
                for f in ("decode_stream.hip", "mfma_attend.h", "sa_internal.h", "plan.h")]
-TRAFFIC_FILE = os.path.join(_ROOT, "profiles", "decode_attention_batch64_ragged_traffic.json")
+# the bench's step workloads: name -> context lengths (after the append)
+HEADLINE = "batch64_8k"
+STEP_WORKLOADS = {"batch64_8k": "8192 for every sequence",
+                  "batch64_ragged": "1 + U{512..8192} per sequence"}
+APPEND_WORKLOADS = ("batch64_8k", "batch64_ragged")
 
 
 def attn_bytes(lens, window, q_heads=64, kv_heads=8, head_dim=64):
@@ -72,11 +84,16 @@ def source_digest():
     return h.hexdigest()
 
 
-def load_traffic():
-    """Per-launch HBM bytes of the dominant call from the committed counter
-    summary, or None if there is none or the kernel sources changed since."""
+def traffic_file(workload):
+    return os.path.join(_ROOT, "profiles", f"decode_attention_{workload}_traffic.json")
+
+
+def load_traffic(workload):
+    """Per-launch HBM bytes of the workload's dominant call from the committed
+    counter summary, or None if there is none or the kernel sources changed
+    since."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -212,21 +229,125 @@ def host_inputs(layer, seqs=None):
                 w=layer.window)
 
 
-def oracle_seconds(hosts, reps, append=True):
-    """Median wall seconds of the fp64 oracle over the given host inputs
-    (append, when asked, then attention), BLAS held to one thread."""
+# ---------------------------------------------------------------------------
+# the fp64 oracle on this host's cores (reported baseline, never the GPU path)
+# ---------------------------------------------------------------------------
+
+_ARRAYS = ("q", "k", "v", "bt", "lens", "kn", "vn", "sinks")
+
+
+def _oracle_warm(_):
+    """Worker start-up: import NumPy and the oracle before anything is timed."""
+    import numpy  # noqa: F401
+    import oracle  # noqa: F401
+    return os.getpid()
+
+
+def _oracle_task(task):
+    """One worker's share of an oracle call: the fp64 oracle's append (when
+    asked) and attention for some sequences and KV heads of a call whose host
+    inputs sit in .npy files (memory-mapped, not copied).  The share's pool
+    blocks and query heads are cut out first (data movement only: the oracle
+    reads the same rows through a remapped table)."""
+    import numpy as np
     import oracle
-    times = []
-    with one_blas_thread():
+    from threadpoolctl import threadpool_limits
+    path, seqs, g0, g1, append, window = task
+    a = {n: np.load(os.path.join(path, n + ".npy"), mmap_mode="r")
+         for n in _ARRAYS if os.path.exists(os.path.join(path, n + ".npy"))}
+    bs = a["k"].shape[3]
+    Hq, Hkv = a["q"].shape[1], a["k"].shape[1]
+    G = Hq // Hkv
+    with threadpool_limits(limits=1):
+        lens = np.asarray(a["lens"])[seqs]
+        bt = np.asarray(a["bt"])[seqs]
+        # table entries covering each sequence's attended slots (the new
+        # token's slot among them)
+        att = [min(int(L), window) if window > 0 else int(L) for L in lens]
+        need = [min(max(1, -(-n // bs)), bt.shape[1]) for n in att]
+        ids = np.concatenate([bt[i, :n] for i, n in enumerate(need)]).astype(np.int64)
+        sub_bt = np.zeros_like(bt)
+        start = 0
+        for i, n in enumerate(need):
+            sub_bt[i, :n] = np.arange(start, start + n)
+            start += n
+        k = np.asarray(a["k"][ids, g0:g1])
+        v = np.asarray(a["v"][ids, g0:g1])
+        q = np.asarray(a["q"])[seqs, g0 * G:g1 * G]
+        sinks = None if "sinks" not in a else np.asarray(a["sinks"])[g0 * G:g1 * G]
+        if append:
+            kn = np.asarray(a["kn"])[seqs, g0:g1]
+            vn = np.asarray(a["vn"])[seqs, g0:g1]
+            k, v = oracle.kv_append(k, v, kn, vn, sub_bt, lens, window)
+        out = oracle.decode_attention(q, k, v, sub_bt, lens, sinks, window)
+    return out
+
+
+class HostOracle:
+    """The fp64 oracle timed on this host's cores: a pool of spawned worker
+    processes (NumPy and the oracle only; BLAS held to one thread in each),
+    every call's sequences (or, for fewer sequences than workers, its
+    (sequence, KV head) pairs) shared out among them.  The inputs are staged
+    once as .npy files that the workers memory-map; the timed region is the
+    pool's whole run over the call."""
+
+    def __init__(self, workers=None):
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        avail = len(os.sched_getaffinity(0))
+        # at most 16: the CPU share of one GPU on the boxes this runs on
+        self.workers = max(1, min(16, avail) if workers is None else workers)
+        self.dir = tempfile.TemporaryDirectory(prefix="sa_oracle_")
+        self.pool = cf.ProcessPoolExecutor(self.workers, mp_context=mp.get_context("spawn"))
+        self.pids = set(self.pool.map(_oracle_warm, range(4 * self.workers)))
+        self.n = 0
+
+    def stage(self, host):
+        """Write one call's host inputs (bench's host_inputs dict); returns a
+        handle for ``seconds``."""
+        import numpy as np
+        path = os.path.join(self.dir.name, f"call{self.n}")
+        self.n += 1
+        os.makedirs(path)
+        for n in _ARRAYS:
+            if host.get(n) is not None:
+                np.save(os.path.join(path, n + ".npy"), np.ascontiguousarray(host[n]))
+        return dict(path=path, B=len(host["lens"]), Hkv=host["k"].shape[1], window=host["w"])
+
+    def tasks(self, staged, append):
+        out = []
+        for c in staged:
+            B, Hkv = c["B"], c["Hkv"]
+            if B >= self.workers:
+                per = -(-B // self.workers)
+                for s0 in range(0, B, per):
+                    out.append((c["path"], list(range(s0, min(B, s0 + per))), 0, Hkv, append,
+                                c["window"]))
+            else:
+                for b in range(B):
+                    for g in range(Hkv):
+                        out.append((c["path"], [b], g, g + 1, append, c["window"]))
+        return out
+
+    def seconds(self, staged, reps=1, append=False):
+        """Median wall seconds of the oracle over the staged calls, run by the
+        whole pool."""
+        tasks = self.tasks(staged, append)
+        times = []
         for _ in range(reps):
             t0 = time.perf_counter()
-            for h in hosts:
-                k, v = h["k"], h["v"]
-                if append:
-                    k, v = oracle.kv_append(k, v, h["kn"], h["vn"], h["bt"], h["lens"], h["w"])
-                oracle.decode_attention(h["q"], k, v, h["bt"], h["lens"], h["sinks"], h["w"])
+            list(self.pool.map(_oracle_task, tasks))
             times.append(time.perf_counter() - t0)
-    return statistics.median(times)
+        return statistics.median(times)
+
+    def describe(self):
+        import numpy as np
+        return (f"NumPy {np.__version__} fp64 oracle, {self.workers} worker processes "
+                f"(BLAS 1 thread each) on {len(os.sched_getaffinity(0))} available cores")
+
+    def close(self):
+        self.pool.shutdown()
+        self.dir.cleanup()
 
 
 def entry(name, what, us, nbytes, cpu_s=None, cpu_note=None, **extra):
@@ -288,8 +409,7 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
     if with_oracle:
         B = first.batch
         seqs = oracle_seqs if oracle_seqs is not None else list(range(B))
-        host = (host_inputs(first, seqs if len(seqs) < B else None), B / len(seqs),
-                1 if len(seqs) * max(first.seq_lens.cpu().tolist()) > 10 ** 5 else 3)
+        host = (host_inputs(first, seqs if len(seqs) < B else None), B / len(seqs), 3)
         note = (f"{len(seqs)} of {B} sequences, scaled x{B / len(seqs):g}" if len(seqs) < B
                 else "every sequence")
     e = entry(label or name, "attention", us, one, input_sets=len(sets), timing=timing,
@@ -431,19 +551,21 @@ def tile_step_config(sa, torch, timer, dev, steps, warmup, variant, T=2, with_or
     return e
 
 
-def add_oracle(e, host):
-    """Time the oracle on the saved host inputs and add it to the entry."""
+def add_oracle(e, host, ho):
+    """Time the oracle (on the host's cores) on the saved host inputs and add
+    it to the entry."""
     h, scale, reps = host
-    cpu_s = oracle_seconds([h], reps, append=False) * scale
+    staged = [ho.stage(h)]
+    ho.seconds(staged)                        # first touch of the staged inputs, untimed
+    cpu_s = ho.seconds(staged, reps) * scale
     e["oracle_s"] = round(cpu_s, 4)
     e["oracle_gbps"] = round(e["bytes"] / cpu_s / 1e9, 4)
-    e["oracle_sample"] += f"; median of {reps}; NumPy fp64, 1 thread"
+    e["oracle_sample"] += f"; median of {reps}; {ho.describe()}"
     e["gpu_speedup_vs_oracle"] = round(cpu_s / (e["us"] * 1e-6), 1)
 
 
 def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=50,
-                       graph=False, oracle_seqs=(0, 21, 42, 63), with_oracle=True,
-                       fused=True):
+                       graph=False, oracle_seqs=(0, 21, 42, 63), ho=None, fused=True):
     """The decode loop: 24 layers alternating ring-128 / paged full attention,
     batch 64, initial lengths 1024..32768, 50 steps each appending one token
     per sequence in every layer.  Timed as whole steps (all layers), eagerly
@@ -501,14 +623,15 @@ def decode_loop_config(sa, torch, timer, dev, stream, variant, layers=24, steps=
     lens.copy_(start_lens)
     us_step = timer.mean_us(runner, steps)
     cpu_step = note = None
-    if with_oracle:
+    if ho is not None:
         lens.copy_(start_lens)
         for m in model:
             m.seq_lens.copy_(lens)
-        hosts = [host_inputs(m, list(oracle_seqs)) for m in model]
-        cpu_step = oracle_seconds(hosts, 1) * B / len(oracle_seqs)
-        note = (f"{len(oracle_seqs)} of {B} sequences, all {layers} layers, one step, scaled "
-                f"x{B / len(oracle_seqs):g}; NumPy fp64, 1 thread")
+        staged = [ho.stage(host_inputs(m, list(oracle_seqs))) for m in model]
+        ho.seconds(staged, append=True)       # first touch, untimed
+        cpu_step = ho.seconds(staged, 1, append=True) * B / len(oracle_seqs)
+        note = (f"{len(oracle_seqs)} of {B} sequences, all {layers} layers (append + "
+                f"attention), one step, scaled x{B / len(oracle_seqs):g}; {ho.describe()}")
     e = entry("decode_loop", f"step ({layers} layers: append + attention each, "
               f"{'one launch' if fused else 'separate append launch'})", us_step,
               total / steps, cpu_step, note, steps=steps, layers=layers,
@@ -571,12 +694,158 @@ def sweep(sa, torch, timer, dev, steps, warmup):
         torch.cuda.empty_cache()
 
 
+def step_calls(sa, torch, dev, workload, variant, separate_append=False):
+    """One step of a workload as its calls in order: (name, algorithmic bytes,
+    launcher(i), input sets).  A layer whose pools would stay in the 256 MB
+    Infinity Cache from one step to the next (the ring layer) rotates over
+    input sets, so that every step reads it from HBM as a model's many layers
+    would; call i of a layer uses set i mod (its sets).  Returns the layers,
+    the calls and each layer's split count."""
+    layers = make_workload(workload, dev)
+    rotations = []
+    for L in layers:
+        pool = L.k_cache.numel() * 4
+        n = 1 if pool > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // max(pool, 1)))
+        rot = [L]
+        if n > 1 and workload == "batch64_ragged":
+            rot += [ragged_layers(dev, seed_offset=101 * i, windows=(L.window,))[0]
+                    for i in range(1, n)]
+        rotations.append(rot)
+    outs = [torch.empty_like(L.q) for L in layers]
+    wss = [sa.new_workspace(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
+                            variant=variant) for L in layers]
+    splits = [sa.num_splits(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
+                            variant=variant) for L in layers]
+    with_append = workload in APPEND_WORKLOADS
+    fused = with_append and not separate_append
+    calls = []
+    for L0, rot, o, ws in zip(layers, rotations, outs, wss):
+        lens = L0.seq_lens.cpu().tolist()
+        nb = attn_bytes(lens, L0.window, L0.q_heads, L0.kv_heads, L0.head_dim)
+        if fused:
+            # the append inside the attention launch (rewriting the same slot
+            # with the same row on every repeat)
+            calls.append((f"append+attention(w={L0.window})", nb + append_bytes(L0.batch),
+                          lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention_append(
+                              L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                              L.seq_lens, L.sinks, L.window, out=o, workspace=ws,
+                              variant=variant))(rot[i % len(rot)]), len(rot)))
+            continue
+        if with_append:
+            calls.append((f"append(w={L0.window})", append_bytes(L0.batch),
+                          lambda i=0, rot=rot: (lambda L: sa.kv_append(
+                              L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
+                              L.seq_lens, L.window))(rot[i % len(rot)]), len(rot)))
+        calls.append((f"attention(w={L0.window})", nb,
+                      lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention(
+                          L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
+                          L.window, out=o, workspace=ws, variant=variant))(rot[i % len(rot)]),
+                      len(rot)))
+    return layers, calls, splits, fused
+
+
+def time_calls(torch, timer, calls, steps, warmup):
+    """Each call alone, K times back to back between two HIP events on its
+    stream (calls under 40 us from a HIP graph of 32 launches instead), with
+    the spread over further rounds and single-call percentiles."""
+    per_call = []
+    for nm, b, f, nsets in calls:
+        timer.settle(f, warmup)
+        us = timer.mean_us(f, steps)
+        timing = "eager, back to back"
+        if us < 40.0:                        # host-bound from Python: replay a graph
+            per_graph = 32
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(per_graph):
+                    f(i)
+            reps = max(2, steps // 10)
+            timer.settle(lambda _: g.replay(), reps)
+            us = timer.mean_us(lambda _: g.replay(), reps) / per_graph
+            timing = f"HIP graph of {per_graph} launches, replayed {reps} times"
+            del g
+        e = dict(call=nm, us_mean=round(us, 2), bytes=b, gbps=round(b / (us * 1e-6) / 1e9, 1),
+                 frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4), timing=timing,
+                 input_sets=nsets)
+        if timing.startswith("eager"):
+            # spread: the same mean over ROUNDS further rounds of back-to-back calls
+            rs = sorted(timer.mean_us(f, steps) for _ in range(ROUNDS))
+            e["rounds"] = dict(rounds=ROUNDS, calls_per_round=steps,
+                               us_median=round(statistics.median(rs), 2),
+                               us_min=round(rs[0], 2), us_max=round(rs[-1], 2))
+            e["per_call_events"] = spread(timer.per_call_us(f, steps))
+        if nsets > 1:
+            e["note"] = (f"{nsets} input sets in rotation (in the step too), so no call finds "
+                         "its inputs in the 256 MB Infinity Cache")
+        per_call.append(e)
+        print(f"# {nm}: {us:.2f} us, {b / (us * 1e-6) / 1e9:.1f} GB/s", flush=True)
+    return per_call
+
+
+KERNEL_NAMES = ("decode_stream_kernel", "combine_stream_kernel", "decode_mfma_kernel",
+                "combine_kernel", "kv_append_kernel")
+
+
+def kernel_times_us(torch, fn, reps):
+    """Mean device duration (us) of each of the library's kernels that fn
+    launches, over reps back-to-back calls, from the PyTorch profiler's device
+    trace (each kernel's own start and end on the GPU); None if the profiler
+    gives no device events here."""
+    try:
+        from torch.profiler import ProfilerActivity, profile
+        torch.cuda.synchronize()
+        with profile(activities=[ProfilerActivity.CUDA]) as prof:
+            for i in range(reps):
+                fn(i)
+            torch.cuda.synchronize()
+        sums, counts = {}, {}
+        for ev in prof.events():
+            name = getattr(ev, "name", "") or ""
+            k = next((n for n in KERNEL_NAMES if n in name), None)
+            dt = getattr(ev, "device_time", None)
+            if dt is None:
+                dt = getattr(ev, "cuda_time", 0.0)
+            if k is None or not dt:
+                continue
+            sums[k] = sums.get(k, 0.0) + float(dt)
+            counts[k] = counts.get(k, 0) + 1
+        if not sums:
+            return None
+        return {k: round(sums[k] / counts[k], 2) for k in sums}
+    except Exception as exc:                  # noqa: BLE001 - report, do not fail the bench
+        print(f"# kernel timing from the profiler unavailable: {exc!r}", flush=True)
+        return None
+
+
+def roofline_of(call, kernels, traffic, split_kernel):
+    """The dominant call's roofline: its algorithmic bytes over its mean
+    event-timed duration (the whole call: decode kernel and, when split, the
+    merge launch), and over the decode kernel's own mean duration from the
+    profiler's device trace."""
+    b, us = call["bytes"], call["us_mean"]
+    achieved = b / (us * 1e-6) / 1e9
+    r = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
+             frac=round(achieved * 1e9 / PEAK_HBM, 4), traffic=traffic,
+             algorithmic_bytes_per_launch=b, avg_launch_us=us,
+             timed="the whole call (every launch it makes), HIP events on its stream")
+    if kernels:
+        k = kernels.get(split_kernel) or kernels.get("decode_mfma_kernel")
+        if k:
+            ka = b / (k * 1e-6) / 1e9
+            r["kernel"] = dict(name=split_kernel if split_kernel in kernels
+                               else "decode_mfma_kernel", us=k, achieved=round(ka, 1),
+                               frac=round(ka * 1e9 / PEAK_HBM, 4),
+                               timed="mean device duration from the profiler's trace")
+        r["kernels_us"] = kernels
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="batch64_ragged")
+    ap.add_argument("--workload", default=HEADLINE, choices=sorted(STEP_WORKLOADS))
     ap.add_argument("--variant", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--oracle-reps", type=int, default=3)
@@ -618,143 +887,67 @@ def main():
         sweep(sa, torch, timer, dev, args.steps, args.warmup)
         return
 
-    layers = make_workload(args.workload, dev)
-    # a layer whose pools would stay in the 256 MB Infinity Cache between steps
-    # (the ring layer) rotates over input sets, so that every step reads it
-    # from HBM as a model's many layers would
-    rotations = []
-    for L in layers:
-        pool = L.k_cache.numel() * 4
-        n = 1 if pool > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // max(pool, 1)))
-        rot = [L]
-        if n > 1 and args.workload == "batch64_ragged":
-            rot += [ragged_layers(dev, seed_offset=101 * i, windows=(L.window,))[0]
-                    for i in range(1, n)]
-        rotations.append(rot)
-    outs = [torch.empty_like(L.q) for L in layers]
-    wss = [sa.new_workspace(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
-                            variant=args.variant) for L in layers]
-    splits = [sa.num_splits(L.q, L.k_cache, L.v_cache, L.block_table, L.window,
-                            variant=args.variant) for L in layers]
-    with_append = args.workload == "batch64_ragged"
-    fused = with_append and not args.separate_append
+    def measure(workload):
+        """Step time, per-call times and the dominant call's roofline of one
+        workload's step; also its host inputs for the oracle."""
+        layers, calls, splits, fused = step_calls(sa, torch, dev, workload, args.variant,
+                                                  args.separate_append)
 
-    # (name, bytes, thunk) in step order; launches go to torch's current stream,
-    # which is the timed stream (and the capture stream while a graph records)
-    # call i of a layer uses input set i mod (its sets); the sets share lengths
-    # and shapes, so bytes, splits and workspace are those of the first
-    calls = []
-    for L0, rot, o, ws in zip(layers, rotations, outs, wss):
-        lens = L0.seq_lens.cpu().tolist()
-        if fused:
-            # the append happens inside the attention launch (rewriting the
-            # same slot with the same row on every repeat)
-            calls.append((f"append+attention(w={L0.window})",
-                          attn_bytes(lens, L0.window, L0.q_heads, L0.kv_heads, L0.head_dim) +
-                          append_bytes(L0.batch),
-                          lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention_append(
-                              L.q, L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
-                              L.seq_lens, L.sinks, L.window, out=o, workspace=ws,
-                              variant=args.variant))(rot[i % len(rot)]), len(rot)))
-            continue
-        if with_append:
-            calls.append((f"append(w={L0.window})", append_bytes(L0.batch),
-                          lambda i=0, rot=rot: (lambda L: sa.kv_append(
-                              L.k_new, L.v_new, L.k_cache, L.v_cache, L.block_table,
-                              L.seq_lens, L.window))(rot[i % len(rot)]), len(rot)))
-        calls.append((f"attention(w={L0.window})",
-                       attn_bytes(lens, L0.window, L0.q_heads, L0.kv_heads, L0.head_dim),
-                       lambda i=0, rot=rot, o=o, ws=ws: (lambda L: sa.decode_attention(
-                           L.q, L.k_cache, L.v_cache, L.block_table, L.seq_lens, L.sinks,
-                           L.window, out=o, workspace=ws, variant=args.variant))(
-                           rot[i % len(rot)]), len(rot)))
+        def step(i=0):
+            for _, _, f, _ in calls:
+                f(i)
+        print(f"# workload {workload}: splits {splits}, warmup {args.warmup}", flush=True)
+        timer.settle(step, args.warmup)
+        # the timed region: exactly K steps, events at its two ends only
+        ms = timer.mean_us(step, args.steps) / 1e3
+        nbytes = sum(b for _, b, _, _ in calls)
+        per_call = time_calls(torch, timer, calls, args.steps, args.warmup)
+        # dominant call: the full-layer attention (the first layer's)
+        dom = next(i for i, c in enumerate(calls) if "attention" in c[0])
+        kernels = kernel_times_us(torch, calls[dom][2], args.steps)
+        split_kernel = ("decode_stream_kernel" if splits[0] > 1 and args.variant in (0, 4, 5)
+                        else "decode_mfma_kernel")
+        traffic = load_traffic(workload) if args.variant == 0 else None
+        roof = roofline_of(per_call[dom], kernels, traffic, split_kernel)
+        roof["call"] = calls[dom][0]
+        hosts = None if args.no_cpu_baseline else [host_inputs(L) for L in layers]
+        info = dict(splits=splits, fused=fused, batch=layers[0].batch,
+                    with_append=workload in APPEND_WORKLOADS)
+        del calls, layers
+        torch.cuda.empty_cache()
+        return ms, nbytes, per_call, roof, hosts, info
 
-    def step(i=0):
-        for _, _, f, _ in calls:
-            f(i)
-
-    print(f"# workload {args.workload}: splits {splits}, warmup {args.warmup}", flush=True)
-    timer.settle(step, args.warmup)
-
-    # the timed region: exactly K steps, events at its two ends only
-    ms_per_step = timer.mean_us(step, args.steps) / 1e3
-    step_bytes = sum(b for _, b, _, _ in calls)
+    ms_per_step, step_bytes, per_call, roofline, main_hosts, info = measure(args.workload)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    # per-call means: each call alone, K times back to back
-    per_call = []
-    for nm, b, f, nsets in calls:
-        timer.settle(f, args.warmup)
-        us = timer.mean_us(f, args.steps)
-        timing = "eager, back to back"
-        if us < 40.0:                        # host-bound from Python: replay a graph
-            per_graph = 32
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                for i in range(per_graph):
-                    f(i)
-            reps = max(2, args.steps // 10)
-            timer.settle(lambda _: g.replay(), reps)
-            us = timer.mean_us(lambda _: g.replay(), reps) / per_graph
-            timing = f"HIP graph of {per_graph} launches, replayed {reps} times"
-            del g
-        e = dict(call=nm, us_mean=round(us, 2), bytes=b, gbps=round(b / (us * 1e-6) / 1e9, 1),
-                 frac_of_peak=round(b / (us * 1e-6) / PEAK_HBM, 4), timing=timing,
-                 input_sets=nsets)
-        if timing.startswith("eager"):
-            # spread: the same mean over ROUNDS further rounds of back-to-back calls
-            n = args.steps
-            rs = sorted(timer.mean_us(f, n) for _ in range(ROUNDS))
-            e["rounds"] = dict(rounds=ROUNDS, calls_per_round=n,
-                               us_median=round(statistics.median(rs), 2),
-                               us_min=round(rs[0], 2), us_max=round(rs[-1], 2))
-            e["per_call_events"] = spread(timer.per_call_us(f, n))
-        if nsets > 1:
-            e["note"] = (f"{nsets} input sets in rotation (in the step too), so no call finds "
-                         "its inputs in the 256 MB Infinity Cache")
-        per_call.append(e)
-        print(f"# {nm}: {us:.2f} us, {b / (us * 1e-6) / 1e9:.1f} GB/s", flush=True)
-
-    # dominant kernel: the full-layer attention call
-    dom = 1 if with_append and not fused else 0
-    dom_us = per_call[dom]["us_mean"]
-    achieved = calls[dom][1] / (dom_us * 1e-6) / 1e9
-    traffic = load_traffic() if args.workload == "batch64_ragged" and args.variant == 0 else None
-    roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
-                    frac=round(achieved * 1e9 / PEAK_HBM, 4), traffic=traffic,
-                    kernel=("decode_stream_kernel + combine_stream_kernel (one attention call"
-                            + (", append inside)" if fused else ")")
-                            if splits[0] > 1 and args.variant in (0, 4) else
-                            "decode_mfma_kernel (+ combine_kernel when split)"),
-                    algorithmic_bytes_per_launch=calls[dom][1], avg_launch_us=round(dom_us, 2))
-
     ceiling = read_ceiling(sa, torch, timer, dev)
-    roofline["frac_of_read_ceiling"] = round(achieved * 1e9 / (ceiling["gbps"] * 1e9), 4)
+    roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling["gbps"], 4)
     print(f"# read ceiling: {ceiling['gbps']} GB/s ({ceiling['frac_of_peak']:.1%} of peak)",
           flush=True)
 
-    main_hosts = None if args.no_cpu_baseline else [host_inputs(L) for L in layers]
-    del calls, layers, rotations, outs, wss
-    torch.cuda.empty_cache()
-
     configs = []
-    headline = None
-    if args.configs == "all" and args.workload == "batch64_ragged":
-        oc = not args.no_cpu_baseline
-        hosts = []
-        for nm, kw in (("batch64_8k", dict(oracle_seqs=[0, 21, 42, 63],
-                                           label="batch64_8k (headline)")),
-                       ("tiny", {}), ("gptoss_layer_8k", {}), ("long_131k_b1", {}),
-                       ("long_131k_b8", dict(oracle_seqs=[3])),
-                       ("long_131k_b8_tp_share", dict(oracle_seqs=[3]))):
+    hosts = []
+    ragged = None
+    oc = not args.no_cpu_baseline
+    if args.configs == "all":
+        if args.workload != "batch64_ragged":
+            r_ms, r_bytes, r_calls, r_roof, r_hosts, r_info = measure("batch64_ragged")
+            ragged = dict(workload="batch64_ragged", call="step: a paged full layer and a "
+                          "sliding-window-128 ring layer, append inside each attention launch",
+                          ms_per_step=round(r_ms, 4), bytes=r_bytes,
+                          value=round(r_bytes / (r_ms * 1e-3) / 1e9, 1), unit="GB/s",
+                          frac_of_peak=round(r_bytes / (r_ms * 1e-3) / PEAK_HBM, 4),
+                          splits=r_info["splits"], us_per_call=r_calls, roofline=r_roof)
+            print(f"# batch64_ragged step: {r_ms * 1e3:.2f} us, {ragged['value']} GB/s",
+                  flush=True)
+        for nm in ("batch64_8k", "tiny", "gptoss_layer_8k", "long_131k_b1", "long_131k_b8",
+                   "long_131k_b8_tp_share"):
             e, h = attention_config(sa, torch, timer, dev, nm, steps=args.steps,
                                     warmup=args.warmup, variant=args.variant, with_oracle=oc,
-                                    **kw)
+                                    label="batch64_8k, attention alone" if nm == "batch64_8k"
+                                    else None)
             configs.append(e)
             hosts.append(h)
             print(f"# {e['config']}: {e['us']} us, {e['gbps']} GB/s", flush=True)
-            if nm == "batch64_8k":
-                headline = e
         rs = rope_step_config(sa, torch, timer, dev, args.steps, args.warmup, args.variant,
                               with_oracle=oc)
         configs.append(rs)
@@ -767,49 +960,56 @@ def main():
         hosts.append(None)
         print(f"# 2-token tile: {ts['us']} us ({ts['us_one_token']} for one token), "
               f"{ts['gbps']} GB/s", flush=True)
+
+    # the oracle on the host's cores, after every GPU timing but the loop's
+    ho = HostOracle() if oc else None
+    if args.configs == "all":
         loop = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=args.graph,
-                                  with_oracle=oc, fused=not args.separate_append)
+                                  ho=ho, fused=not args.separate_append)
         configs.append(loop)
-        hosts.append(None)                   # (its oracle is timed inside decode_loop_config)
         print(f"# decode loop: {loop['us']} us per step, {loop['gbps']} GB/s", flush=True)
         if not args.graph:                   # the same loop replayed from a HIP graph per step
             gl = decode_loop_config(sa, torch, timer, dev, stream, args.variant, graph=True,
-                                    with_oracle=False, fused=not args.separate_append)
+                                    ho=None, fused=not args.separate_append)
             gl["config"] = "decode_loop (HIP graph)"
             configs.append(gl)
-            hosts.append(None)
             print(f"# decode loop, HIP graph: {gl['us']} us per step, {gl['gbps']} GB/s",
                   flush=True)
-        if oc:                               # host timings after all GPU timings
+        if oc:
             print("# timing the oracle on the configurations...", flush=True)
             for e, h in zip(configs, hosts):
                 if h is not None:
-                    add_oracle(e, h)
+                    add_oracle(e, h, ho)
 
     cpu = None
-    if main_hosts is not None:
+    if ho is not None:
         print("# timing the oracle on the step...", flush=True)
-        sec = oracle_seconds(main_hosts, args.oracle_reps, append=with_append)
-        import numpy as np
-        cpu = dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
-                   seconds_per_step=round(sec, 3),
-                   sample=f"the whole {args.workload} step (every sequence, every layer), "
-                          f"median of {args.oracle_reps} runs, NumPy {np.__version__} fp64, "
-                          f"BLAS 1 thread")
+        staged = [ho.stage(h) for h in main_hosts]
+        ho.seconds(staged, append=info["with_append"])          # first touch, untimed
+        sec = ho.seconds(staged, args.oracle_reps, append=info["with_append"])
+        cpu = dict(value=round(step_bytes / sec / 1e9, 4), unit="GB/s", cores=ho.workers,
+                   kind="oracle", seconds_per_step=round(sec, 3), blas_threads_per_core=1,
+                   cores_available=len(os.sched_getaffinity(0)),
+                   sample=f"the whole {args.workload} step (every sequence"
+                          f"{', append then attention' if info['with_append'] else ''}), "
+                          f"median of {args.oracle_reps} runs; {ho.describe()}")
+        ho.close()
 
+    wl = STEP_WORKLOADS[args.workload]
     res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_per_step, 4), higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic",
-               config=dict(workload=args.workload, batch=64, q_heads=64, kv_heads=8, head_dim=64,
-                           block_size=16, splits=splits, variant=args.variant,
-                           step=("append inside attention, one launch per layer" if fused
-                                 else "append + attention per layer" if with_append
+               config=dict(workload=args.workload, batch=info["batch"], q_heads=64, kv_heads=8,
+                           head_dim=64, block_size=16, context=wl, splits=info["splits"],
+                           variant=args.variant,
+                           step=("append inside attention, one launch per layer (plus the "
+                                 "merge launch of a split call)" if info["fused"]
+                                 else "append + attention per layer" if info["with_append"]
                                  else "attention")),
                us_per_call=per_call, step_bytes=step_bytes,
                frac_of_peak=round(value * 1e9 / PEAK_HBM, 4),
                roofline=roofline, cpu_baseline=cpu, read_ceiling=ceiling,
-               headline_uniform_8k=headline,
-               configs=configs)
+               batch64_ragged_step=ragged, configs=configs)
     print(json.dumps(res), flush=True)
 
 

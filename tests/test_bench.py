@@ -50,3 +50,36 @@ def test_more_than_one_gpu_is_refused():
 def test_spread_percentiles():
     s = bench.spread([float(i) for i in range(1, 101)])
     assert s == dict(calls=100, us_median=50.5, us_p10=10.9, us_p90=90.1)
+
+
+class _Pool:
+    """HostOracle.tasks needs only the worker count."""
+    def __init__(self, workers):
+        self.workers = workers
+
+
+def test_oracle_tasks_cover_every_sequence_and_head_once():
+    for workers, B, Hkv in ((16, 64, 8), (16, 1, 8), (8, 8, 1), (16, 5, 2), (3, 64, 8)):
+        c = dict(path="p", B=B, Hkv=Hkv, window=0)
+        seen = []
+        for path, seqs, g0, g1, append, window in bench.HostOracle.tasks(_Pool(workers), [c],
+                                                                           True):
+            assert path == "p" and append and window == 0
+            seen += [(b, g) for b in seqs for g in range(g0, g1)]
+        assert sorted(seen) == [(b, g) for b in range(B) for g in range(Hkv)]
+
+
+def test_oracle_task_runs_the_oracle_on_its_share(tmp_path):
+    """A worker's share gives the oracle's own output for those sequences and
+    heads (the task only cuts out data): run in-process here."""
+    import numpy as np
+    import oracle
+    L = synth.make_layer(batch=3, q_heads=8, kv_heads=2, lens=[40, 70, 17], seed=3)
+    h = bench.host_inputs(L)
+    for n in bench._ARRAYS:
+        if h.get(n) is not None:
+            np.save(tmp_path / (n + ".npy"), np.ascontiguousarray(h[n]))
+    got = bench._oracle_task((str(tmp_path), [0, 2], 1, 2, True, 0))
+    k, v = oracle.kv_append(h["k"], h["v"], h["kn"], h["vn"], h["bt"], h["lens"], 0)
+    want = oracle.decode_attention(h["q"], k, v, h["bt"], h["lens"], h["sinks"], 0)
+    assert np.array_equal(got, want[[0, 2]][:, 4:8])      # KV head 1: query heads 4..7
