@@ -18,7 +18,9 @@ namespace {
 
 using namespace mfma;
 
-template <int BSL, bool ROPE, bool MULTI>
+// DEPTH: the step pipeline (2, or kBurst: every step of a partition of at
+// most kBurst steps loaded at once).
+template <int BSL, bool ROPE, bool MULTI, int DEPTH>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
     const int c16 = lane & 15;
@@ -30,16 +32,41 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int g = bg - b * a.Hkv;
     const Col col = column(a, lane);
     const bool head_ok = col.ok;
+    const int P = a.part_tokens;
+    const int t0 = split * P;
+
+    // The partition's slots follow from the grid alone, so the loads that
+    // do not depend on the sequence's length (the query, the first table
+    // slice, the new token's words) go out with the length's load, not after
+    // its wait.
+    u32x4_t qop0, qop1;
+    if (!ROPE) load_query<false>(a, b, g, lane, qop0, qop1);
+    Unit u = make_unit(a, b, g, lane);
+    const RunStart pre = run_start<BSL>(u, t0, lane);
 
     const int L = a.seq_lens[b];
     int n = L;
     if (a.window > 0) n = min(n, a.window);
     n = max(0, min(n, a.mbs << a.bs_log2));
-    const int P = a.part_tokens;
-    const int t0 = split * P;
     const size_t bh = col_row(a, b, g, col);       // this lane's (token, head) row
 
-    if (t0 >= n) {
+    // A partition past the context attends one slot at t0 (inside its
+    // table's allocated entries: a partition starts below the capacity) and
+    // drops the result, instead of returning early: a branch here would let
+    // the compiler sink the loads above past the length's wait.  Its run holds
+    // no new token's slot (those lie below the context end), so it stores
+    // nothing.
+    const bool active = t0 < n;                    // wave-uniform
+    const int t1 = active ? min(n, t0 + P) : t0 + 1;
+    const int pos = ROPE && L > 0 ? rope_row(a, L) : 0;
+    if (ROPE) load_query<true>(a, b, g, lane, qop0, qop1, pos);
+    u.new_slot = MULTI ? -1 : new_token_slot(a, L, n);
+    u.rope_pos = pos;
+    u.L = L;
+    State st;
+    st.reset();
+    attend<BSL, ROPE, MULTI, DEPTH>(a, u, t0, t1, qop0, qop1, st, pre);
+    if (!active) {
         if (a.mode == kWritePartials) {
             if (head_ok && q4 == 0) a.part_lse[bh * a.num_splits + split] = -INFINITY;
         } else if (split == 0) {
@@ -47,15 +74,6 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
         }
         return;
     }
-    const int t1 = min(n, t0 + P);
-
-    u32x4_t qop0, qop1;
-    const int pos = ROPE ? rope_row(a, L) : 0;
-    load_query<ROPE>(a, b, g, lane, qop0, qop1, pos);
-    const Unit u = make_unit(a, b, g, lane, MULTI ? -1 : new_token_slot(a, L, n), pos, L);
-    State st;
-    st.reset();
-    attend<BSL, ROPE, MULTI>(a, u, t0, t1, qop0, qop1, st);
     const float l_tot = st.total();
 
     if (a.mode == kWriteOut) {
@@ -103,23 +121,30 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     }
 }
 
-template <bool ROPE, bool MULTI>
+template <bool ROPE, bool MULTI, int DEPTH>
 hipError_t launch_static(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hkv * a.num_splits);
     switch (a.bs_log2) {
-        case 3: return launch(decode_mfma_kernel<3, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
-        case 4: return launch(decode_mfma_kernel<4, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
-        case 5: return launch(decode_mfma_kernel<5, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
-        case 6: return launch(decode_mfma_kernel<6, ROPE, MULTI>, grid, dim3(64), 0, stream, a);
+        case 3: return launch(decode_mfma_kernel<3, ROPE, MULTI, DEPTH>, grid, dim3(64), 0, stream, a);
+        case 4: return launch(decode_mfma_kernel<4, ROPE, MULTI, DEPTH>, grid, dim3(64), 0, stream, a);
+        case 5: return launch(decode_mfma_kernel<5, ROPE, MULTI, DEPTH>, grid, dim3(64), 0, stream, a);
+        case 6: return launch(decode_mfma_kernel<6, ROPE, MULTI, DEPTH>, grid, dim3(64), 0, stream, a);
         default: return hipErrorInvalidValue;
     }
 }
 
+template <int DEPTH>
+hipError_t launch_static_depth(const DecodeArgs& a, bool rope, hipStream_t stream) {
+    if (a.T > 1) return rope ? hipErrorInvalidValue : launch_static<false, true, DEPTH>(a, stream);
+    return rope ? launch_static<true, false, DEPTH>(a, stream)
+                : launch_static<false, false, DEPTH>(a, stream);
+}
+
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream) {
-    if (a.T > 1) return rope ? hipErrorInvalidValue : launch_static<false, true>(a, stream);
-    return rope ? launch_static<true, false>(a, stream) : launch_static<false, false>(a, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, bool burst, hipStream_t stream) {
+    return burst ? launch_static_depth<kBurst>(a, rope, stream)
+                 : launch_static_depth<2>(a, rope, stream);
 }
 
 }  // namespace sa

@@ -153,6 +153,9 @@ struct StepRegs {
     u32x4_t v[4];   // dim tile j
 };
 
+// Pipeline depth that issues every step of a short run at once (attend_run).
+constexpr int kBurst = kBurstSteps;
+
 // Online-softmax state of one wavefront: acc[j] lane (head c16, q4) holds dims
 // 16j + 4*q4 .. +3 of that head; m is the reference max of the exponents
 // (log2 domain, equal on the head's four lanes; at most kRescaleSlack below the
@@ -514,6 +517,25 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         }
     }
 
+    if constexpr (DEPTH == kBurst) {
+        // Runs of up to kBurst steps issue every step's loads at once (steps
+        // past the run re-read its last chunk, which the clamp in load_step
+        // keeps inside the run's blocks, and are never computed): one round
+        // trip of K/V instead of a pipeline's several, for calls whose
+        // partitions are short.  Longer runs take the two-step pipeline.
+        if (nsteps <= kBurst) {
+            StepRegs R[kBurst];
+            load_step(0, R[0]);
+            if (stores_new && !new_first) store_new();
+#pragma unroll
+            for (int s = 1; s < kBurst; ++s) load_step(s, R[s]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < kBurst; ++s)
+                if (s < nsteps) compute_step(s, R[s]);
+            return;
+        }
+    }
     if constexpr (DEPTH == 3) {
         // Three register sets: the loads of steps s+1 and s+2 are in flight
         // while step s computes (for a kernel that runs one wavefront per
@@ -607,14 +629,33 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
 // token's words are read here, with no branch, so they travel with the
 // caller's query loads.
 // DEPTH: register sets of the step pipeline (2, or 3 for one wavefront per SIMD).
+// The loads that begin a unit's run of slots from t0: its first table slice
+// and this lane's words of the new token's K and V rows.  None of them
+// depends on the sequence's length, so a caller may issue them before it
+// waits for that.
+struct RunStart {
+    TableSlice tbl;
+    unsigned kword;
+    uint16_t vval;
+};
+template <int BSL>
+__device__ __forceinline__ RunStart run_start(const Unit& u, int t0, int lane) {
+    RunStart r;
+    r.tbl = table_slice(u, t0 >> BSL, lane);
+    r.kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
+    r.vval = u.vn_row[lane];
+    return r;
+}
+
 template <int BSL, bool ROPE, bool MULTI = false, int DEPTH = 2>
 __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t0, int t1,
-                                       u32x4_t qop0, u32x4_t qop1, State& st) {
+                                       u32x4_t qop0, u32x4_t qop1, State& st,
+                                       const RunStart& pre) {
     constexpr int run = kMaxTableSlice << BSL;
     const int lane = u.c16 + 16 * u.q4;
-    TableSlice tbl = table_slice(u, t0 >> BSL, lane);
-    const unsigned kword = reinterpret_cast<const unsigned*>(u.kn_row)[lane & 31];
-    const uint16_t vval = u.vn_row[lane];
+    TableSlice tbl = pre.tbl;
+    const unsigned kword = pre.kword;
+    const uint16_t vval = pre.vval;
     // cos / sin of the pairs of this lane's new-key word (read with no branch)
     float2 kcos = {1.f, 1.f}, ksin = {0.f, 0.f};
     if (ROPE) {
@@ -636,6 +677,12 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t
         r0 = r1;
         tbl = table_slice(u, r0 >> BSL, lane);
     }
+}
+template <int BSL, bool ROPE, bool MULTI = false, int DEPTH = 2>
+__device__ __forceinline__ void attend(const DecodeArgs& a, const Unit& u, int t0, int t1,
+                                       u32x4_t qop0, u32x4_t qop1, State& st) {
+    attend<BSL, ROPE, MULTI, DEPTH>(a, u, t0, t1, qop0, qop1, st,
+                                    run_start<BSL>(u, t0, u.c16 + 16 * u.q4));
 }
 
 // bf16 output of the unit's heads with the sink in the denominator:

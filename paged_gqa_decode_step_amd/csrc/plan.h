@@ -23,9 +23,12 @@ int query_tokens(const sa_dims* d) { return d->num_query_tokens > 0 ? d->num_que
 // timing).  A partition is 32 * 2^k slots, at most kMaxTableSlice blocks and
 // at most kMaxPartTokens slots, and never longer than the context capacity
 // (a 128-slot ring is one partition).  It halves, down to kMinPartTokens,
-// while a call would have fewer than kMinWaves partition wavefronts.  Chosen
-// from measured sweeps on MI355X: long partitions keep the partial traffic
-// and the combine small; batch-1 calls trade some of that for parallelism.
+// while a call would have fewer than kMinWaves partition wavefronts.  A call
+// whose grid of kBurstSteps-step partitions is at most one wavefront per SIMD
+// takes those instead (the static kernel then loads a whole partition at
+// once).  Chosen from measured sweeps on MI355X: long partitions keep the
+// partial traffic and the combine small; batch-1 calls trade some of that
+// for parallelism.
 constexpr int kMaxPartTokens = 1024;
 constexpr int kMinPartTokens = 256;
 constexpr long kMinWaves = 128;
@@ -50,9 +53,6 @@ constexpr long kWaveQuantum = 512;
 constexpr long kMaxSegsPerUnit = 128;
 constexpr long kMinStreamSteps = 8;
 constexpr int kMaxStreamSeqs = 2048;
-// partitions per row up to which the static combine reads every partial at
-// once (its one-wavefront form)
-constexpr int kStaticMergeSplits = 8;
 
 struct Plan {
     int32_t splits;
@@ -74,11 +74,17 @@ Plan plan(const sa_dims* d, int32_t window) {
         P = (int)(want < gran ? gran : (want > pmax ? pmax : want));
     } else {
         const long units = (long)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
-        P = pmax;
-        while (P / 2 >= gran && P / 2 >= max_n) P /= 2;          // one partition covers it
-        while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
-               units * ((max_n + P - 1) / P) < kMinWaves)
-            P /= 2;
+        const int pb = sa::kBurstSteps * sa::kStepTokens;
+        if (max_n > pb && pb >= gran && pb <= pmax &&
+            units * ((max_n + pb - 1) / pb) <= kStreamWaves) {
+            P = pb;                                              // burst partitions
+        } else {
+            P = pmax;
+            while (P / 2 >= gran && P / 2 >= max_n) P /= 2;      // one partition covers it
+            while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
+                   units * ((max_n + P - 1) / P) < kMinWaves)
+                P /= 2;
+        }
     }
     Plan p;
     p.part_tokens = P;
@@ -129,6 +135,22 @@ long stream_waves(const sa_dims* d, int32_t window) {
     return nw < 1 ? 1 : nw;
 }
 
+// The static kernel loads every step of its partition at once when
+// partitions are kBurstSteps steps and the grid is at most one
+// wavefront per SIMD (the burst kernels hold all those steps in registers,
+// so they run one wavefront per SIMD): one round trip of K/V per partition,
+// for calls too small to keep HBM busy with pipelined wavefronts.
+#ifndef SA_STATIC_BURST
+#define SA_STATIC_BURST 1
+#endif
+bool static_burst(const sa_dims* d, const Plan& p) {
+    if (!SA_STATIC_BURST) return false;
+    // exactly kBurstSteps steps a partition: shorter ones (the ring layer's
+    // 4) measured slower with the burst's unused loads than pipelined
+    return p.part_tokens == sa::kBurstSteps * sa::kStepTokens &&
+           (long long)d->num_seqs * d->num_kv_heads * p.splits <= kStreamWaves;
+}
+
 // Which kernel a call with these dims uses (assumes check_dims passed).
 Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
     // the balanced kernel keeps its per-sequence table in LDS and walks steps
@@ -148,20 +170,21 @@ Mode choose_mode(const sa_dims* d, int32_t window, const Plan& p) {
         case SA_VARIANT_VALU:
             return Mode::kStatic;
         default: {
-            // one static partition needs no merge at all; nor is the balanced
-            // kernel worth its fixed costs (the length scan, the merge's
-            // segment records) when the static grid holds between half and one
-            // wavefront per SIMD and the static merge reads every partial of a
-            // row in one round trip (at most kStaticMergeSplits): then every
-            // partition runs at once (measured on MI355X: 0.2-2.8 us faster
-            // from batch 8 x 8192 to 64 x 2048, uniform or ragged; with fewer
-            // partitions than that the GPU is not filled, with more the
-            // balanced kernel's even split wins); beyond that the balanced
-            // kernel keeps every compute unit equally busy
+            // One static partition needs no merge at all.  Nor is the balanced
+            // kernel worth its fixed costs when the static grid is burst
+            // partitions, or holds between half and one wavefront per SIMD:
+            // the length scan before any load (the static kernel issues its
+            // first loads with the length's), and the merge's segment records
+            // (the static merge knows where every partial is and reads them
+            // all in one round trip).  Every partition then runs at once
+            // (measured on MI355X: batch 1 x 8192 8.4 vs 9.7 us, batch 1 x
+            // 131072 45.6 vs 47.4 us, 0.2-2.8 us faster from batch 8 x 8192 to
+            // 64 x 2048); with fewer, longer partitions the GPU is not kept
+            // busy, with more the balanced kernel's even split wins.
             if (d->num_splits > 0 || p.splits == 1 || !fits_stream) return Mode::kStatic;
+            if (static_burst(d, p)) return Mode::kStatic;
             const long parts = (long)d->num_seqs * d->num_kv_heads * p.splits;
-            if (p.splits <= kStaticMergeSplits && parts >= kStreamWaves / 2 && parts <= kStreamWaves)
-                return Mode::kStatic;
+            if (parts >= kStreamWaves / 2 && parts <= kStreamWaves) return Mode::kStatic;
             return Mode::kBalanced;
         }
     }

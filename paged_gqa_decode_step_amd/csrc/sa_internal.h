@@ -23,6 +23,7 @@ constexpr int kMaxGroup = 16;      // query columns per KV head: (query tokens) 
                                    // per KV head) fill one 16-column MFMA tile
 constexpr int kStepTokens = 32;    // tokens per inner step of the partition kernels
 constexpr int kMaxTableSlice = 64; // block-table entries one partition may span
+constexpr int kBurstSteps = 8;     // steps of a partition the burst kernels load at once
 
 struct AppendArgs {
     const uint16_t* k_new;
@@ -97,7 +98,9 @@ hipError_t scratch_pointer(void** out);
 hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // rope: the kernels built with the rotary embedding of q and k_new; a.T > 1:
 // the kernels built for several causal query tokens per sequence
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, hipStream_t stream);
+// burst: the kernels that load every step of a partition of at most 8 steps
+// at once (for grids of short partitions)
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, bool burst, hipStream_t stream);
 // fused_merge: the last wavefront of a split unit merges it (part_o holds the
 // segments, counters the arrivals); otherwise a merge launch follows, reading
 // part_o / part_lse and the unit records in unit_seg

@@ -262,10 +262,10 @@ def test_binding_checks_the_pool_layouts():
 
 
 def test_small_grids_of_few_partitions_take_the_static_split(lib):
-    """A static grid of 512 to 1024 partitions with at most 8 per (sequence,
-    KV head) runs the static split (its workspace holds S partials for every
-    output row); a smaller or larger grid, the balanced kernel (two partial
-    slots per wavefront of 1024)."""
+    """A static grid of 8-step partitions that fits one wavefront per SIMD, or
+    of 512 to 1024 partitions, runs the static split (its workspace holds S
+    partials for every output row); any other grid, the balanced kernel (two
+    partial slots per wavefront of 1024)."""
     counters = (1 << 18) * 4
 
     def ws(B, mbs, S, variant=0):
@@ -274,22 +274,31 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
         assert lib.sa_decode_num_splits(ctypes.byref(d), 0) == S
         return lib.sa_decode_workspace_bytes(ctypes.byref(d), 0)
 
+    def a256(x):                                         # regions start 256-byte aligned
+        return (x + 255) & ~255
+
     def static(B, S):
         rows = B * 64 * S                                # B x Hq x S
-        return counters + rows * 64 * 4 + rows * 4 + B * 8 * 2 * 4
+        return counters + a256(rows * 64 * 4) + a256(rows * 4) + a256(B * 8 * 2 * 4)
 
     def balanced(B):
         rows = 1024 * 2 * 8                              # wavefronts x 2 slots x G
-        return counters + rows * 64 * 4 + rows * 4 + B * 8 * 2 * 4
+        return counters + a256(rows * 64 * 4) + a256(rows * 4) + a256(B * 8 * 2 * 4)
 
     def balanced_last_merges(B):
         return counters + 1024 * 2 * 17 * 64 * 4        # wavefronts x 2 segment slots
     assert ws(64, 128, 2) == static(64, 2)               # 1024 partitions
     assert ws(8, 512, 8) == static(8, 8)                 # 512
+
+    assert ws(1, 512, 32) == static(1, 32)               # 256: batch 1 x 8192
+    assert ws(1, 8192, 128) == static(1, 128)            # 1024: batch 1 x 131072
     assert ws(128, 128, 2) == balanced(128)              # 2048
-    assert ws(4, 512, 8) == balanced(4)                  # 256
+    assert ws(1, 128, 8) == static(1, 8)                 # 64 burst partitions
+    assert ws(2, 512, 32) == static(2, 32)               # 512 burst partitions
+    assert ws(4, 512, 32) == static(4, 32)               # 1024 burst partitions
+    assert ws(3, 1024, 16) == balanced(3)                # 384 partitions of 32 steps
     assert ws(128, 128, 2, variant=5) == balanced_last_merges(128)
-    assert ws(4, 512, 8, variant=4) == balanced(4)
+    assert ws(4, 512, 32, variant=4) == balanced(4)
 
 
 def test_plain_row_pools_are_refused_not_misread(lib):
