@@ -859,6 +859,10 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only time the fused step of a paged full layer over a grid of batch "
                          "sizes and context lengths (one JSON line per point) and exit")
+    ap.add_argument("--only", default="", metavar="CONFIG[,CONFIG...]",
+                    help="only time these attention configurations (tiny, gptoss_layer_8k, "
+                         "long_131k_b1, long_131k_b8, long_131k_b8_tp_share, batch64_8k), one "
+                         "JSON line each, and exit (for profiling them)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES, three times, and exit: the "
                          "reference for scaling rocprofv3's FETCH_SIZE / WRITE_SIZE")
@@ -885,6 +889,12 @@ def main():
     timer = Timer(torch, stream)
     if args.sweep:
         sweep(sa, torch, timer, dev, args.steps, args.warmup)
+        return
+    if args.only:
+        for nm in args.only.split(","):
+            e, _ = attention_config(sa, torch, timer, dev, nm, steps=args.steps,
+                                    warmup=args.warmup, variant=args.variant, with_oracle=False)
+            print(json.dumps(e), flush=True)
         return
 
     def measure(workload):
