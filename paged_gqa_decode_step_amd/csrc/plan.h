@@ -23,9 +23,9 @@ int query_tokens(const sa_dims* d) { return d->num_query_tokens > 0 ? d->num_que
 // timing).  A partition is 32 * 2^k slots, at most kMaxTableSlice blocks and
 // at most kMaxPartTokens slots, and never longer than the context capacity
 // (a 128-slot ring is one partition).  It halves, down to kMinPartTokens,
-// while a call would have fewer than kMinWaves partition wavefronts.  A call
-// whose grid of kBurstSteps-step partitions is at most one wavefront per SIMD
-// takes those instead (the static kernel then loads a whole partition at
+// while a call would have fewer than kMinWaves partition wavefronts.  A split
+// call whose grid of kBurstSteps-step partitions is at most one wavefront per
+// SIMD takes those instead (the static kernel then loads a whole partition at
 // once).  Chosen from measured sweeps on MI355X: long partitions keep the
 // partial traffic and the combine small; batch-1 calls trade some of that
 // for parallelism.
@@ -74,17 +74,17 @@ Plan plan(const sa_dims* d, int32_t window) {
         P = (int)(want < gran ? gran : (want > pmax ? pmax : want));
     } else {
         const long units = (long)(d->num_seqs > 0 ? d->num_seqs : 1) * d->num_kv_heads;
+        P = pmax;
+        while (P / 2 >= gran && P / 2 >= max_n) P /= 2;          // one partition covers it
+        while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
+               units * ((max_n + P - 1) / P) < kMinWaves)
+            P /= 2;
+        // a call that is split anyway takes burst partitions when their grid
+        // fits (a call of one partition a unit needs no merge at all)
         const int pb = sa::kBurstSteps * sa::kStepTokens;
-        if (max_n > pb && pb >= gran && pb <= pmax &&
-            units * ((max_n + pb - 1) / pb) <= kStreamWaves) {
-            P = pb;                                              // burst partitions
-        } else {
-            P = pmax;
-            while (P / 2 >= gran && P / 2 >= max_n) P /= 2;      // one partition covers it
-            while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
-                   units * ((max_n + P - 1) / P) < kMinWaves)
-                P /= 2;
-        }
+        if (max_n > P && pb >= gran && pb <= pmax &&
+            units * ((max_n + pb - 1) / pb) <= kStreamWaves)
+            P = pb;
     }
     Plan p;
     p.part_tokens = P;
