@@ -424,19 +424,37 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
 
 
 def read_ceiling(sa, torch, timer, dev, nbytes=4 << 30):
-    """The practical HBM read ceiling: the library's plain streaming-read probe
-    over a 4 GiB buffer (far past the Infinity Cache)."""
+    """The practical HBM read ceilings: the library's plain streaming-read
+    probe over a 4 GiB buffer (far past the Infinity Cache), and its
+    scattered-tile probe (the decode kernels' pattern: 2 KiB tiles at random
+    places, 1024 wavefronts, 8 KiB steps, three in flight; 1 GiB a call from
+    four disjoint sets of tiles in rotation)."""
+    import numpy as np
     x = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     x.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
     f = lambda _=0: sa.read_bandwidth_probe(x, sink)                      # noqa: E731
     timer.settle(f, 5)
     us = timer.mean_us(f, 20)
-    del x
+    stream = dict(kernel="sa_read_bandwidth_probe (16-byte non-temporal streaming read)",
+                  bytes=nbytes, us=round(us, 1), gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
+                  frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4))
+    ntotal = nbytes // 2048
+    perm = np.random.default_rng(7).permutation(ntotal).astype(np.int32)
+    nsets = 4
+    per = ntotal // nsets
+    sets = [torch.from_numpy(perm[i * per:(i + 1) * per].copy()).to(dev) for i in range(nsets)]
+    g = lambda i=0: sa.read_tiles_probe(x, sets[i % nsets], sink, waves=1024)   # noqa: E731
+    timer.settle(g, 8)
+    tus = timer.mean_us(g, 20)
+    tb = per * 2048
+    tiles = dict(kernel="sa_read_tiles_probe (2 KiB tiles at random places, the decode "
+                        "kernels' read pattern with no arithmetic, 1024 wavefronts)",
+                 bytes=tb, us=round(tus, 1), gbps=round(tb / (tus * 1e-6) / 1e9, 1),
+                 frac_of_peak=round(tb / (tus * 1e-6) / PEAK_HBM, 4))
+    del x, sets
     torch.cuda.empty_cache()
-    return dict(kernel="sa_read_bandwidth_probe (16-byte non-temporal streaming read)",
-                bytes=nbytes, us=round(us, 1), gbps=round(nbytes / (us * 1e-6) / 1e9, 1),
-                frac_of_peak=round(nbytes / (us * 1e-6) / PEAK_HBM, 4))
+    return dict(stream, scattered_tiles=tiles)
 
 
 def rope_step_config(sa, torch, timer, dev, steps, warmup, variant, with_oracle=True):
@@ -931,8 +949,10 @@ def main():
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     ceiling = read_ceiling(sa, torch, timer, dev)
     roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / ceiling["gbps"], 4)
-    print(f"# read ceiling: {ceiling['gbps']} GB/s ({ceiling['frac_of_peak']:.1%} of peak)",
-          flush=True)
+    roofline["frac_of_tile_ceiling"] = round(
+        roofline["achieved"] / ceiling["scattered_tiles"]["gbps"], 4)
+    print(f"# read ceiling: {ceiling['gbps']} GB/s ({ceiling['frac_of_peak']:.1%} of peak); "
+          f"scattered tiles {ceiling['scattered_tiles']['gbps']} GB/s", flush=True)
 
     configs = []
     hosts = []

@@ -331,6 +331,21 @@ int sa_combine(const float* part_o, const float* part_lse, const float* sinks,
  */
 int sa_read_bandwidth_probe(const void* data, size_t bytes, uint32_t* sink, void* stream);
 
+/*
+ * Measurement helper, not a step of the decode path: the decode kernels'
+ * read pattern with no arithmetic.  tiles[0..ntiles) are tile numbers; tile k
+ * is the 2048 bytes at data + 2048 k (one (block, KV head) piece of a pool at
+ * block size 16).  waves one-wavefront workgroups each read a contiguous
+ * stretch of the list as the balanced decode kernel walks its steps: 8 KiB
+ * (four tiles) a step, three steps of loads in flight, non-temporal 16-byte
+ * loads, the tile numbers fetched 64 at a time.  Every 32-bit word of every
+ * listed tile is XORed into *sink once per listing.  Tile numbers outside
+ * [0, bytes / 2048) are clamped into it.  data 16-byte aligned; waves in
+ * [1, 65535]; ntiles = 0 launches nothing.
+ */
+int sa_read_tiles_probe(const void* data, size_t bytes, const int32_t* tiles, int64_t ntiles,
+                        int32_t waves, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* sa_status_string(int status);
 

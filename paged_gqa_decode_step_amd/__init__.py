@@ -80,7 +80,7 @@ EXPORTS = ("sa_kv_append", "sa_decode_num_splits", "sa_decode_workspace_bytes",
            "sa_decode_attention", "sa_decode_attention_append",
            "sa_decode_attention_append_noalloc", "sa_decode_attention_append_rope",
            "sa_decode_partials",
-           "sa_combine", "sa_read_bandwidth_probe", "sa_status_string")
+           "sa_combine", "sa_read_bandwidth_probe", "sa_read_tiles_probe", "sa_status_string")
 
 
 def load(path: Optional[str] = None):
@@ -118,6 +118,8 @@ def load(path: Optional[str] = None):
     lib.sa_combine.restype = ctypes.c_int
     lib.sa_read_bandwidth_probe.argtypes = [vp, sz, vp, vp]
     lib.sa_read_bandwidth_probe.restype = ctypes.c_int
+    lib.sa_read_tiles_probe.argtypes = [vp, sz, vp, ctypes.c_int64, i32, vp, vp]
+    lib.sa_read_tiles_probe.restype = ctypes.c_int
     lib.sa_status_string.argtypes = [ctypes.c_int]
     lib.sa_status_string.restype = ctypes.c_char_p
     if path is None:
@@ -470,3 +472,18 @@ def read_bandwidth_probe(data, sink, stream=None):
         st = load().sa_read_bandwidth_probe(_ptr(data), nbytes, _ptr(sink),
                                             _stream(stream, data.device))
     _raise(st, "sa_read_bandwidth_probe")
+
+
+def read_tiles_probe(data, tiles, sink, waves=1024, stream=None):
+    """Read the 2 KiB tiles of ``data`` that ``tiles`` (int32 tile numbers)
+    lists, in the decode kernels' pattern, XOR-folding their 32-bit words into
+    ``sink`` (int32 device tensor, one element, start value set by the caller)."""
+    if not isinstance(data, torch.Tensor) or not data.is_cuda or not data.is_contiguous():
+        raise ValueError("data must be a contiguous GPU tensor")
+    _check(tiles, "tiles", torch.int32, 1, data.device)
+    _check(sink, "sink", torch.int32, 1, data.device)
+    nbytes = data.numel() * data.element_size()
+    with _on(data.device):
+        st = load().sa_read_tiles_probe(_ptr(data), nbytes, _ptr(tiles), tiles.numel(), int(waves),
+                                        _ptr(sink), _stream(stream, data.device))
+    _raise(st, "sa_read_tiles_probe")

@@ -339,6 +339,17 @@ int sa_read_bandwidth_probe(const void* data, size_t bytes, uint32_t* sink, void
     return to_status(sa::launch_read_probe(data, bytes, sink, (hipStream_t)stream));
 }
 
+int sa_read_tiles_probe(const void* data, size_t bytes, const int32_t* tiles, int64_t ntiles,
+                        int32_t waves, uint32_t* sink, void* stream) {
+    if (!sink || ntiles < 0 || waves < 1 || waves > 65535 || !aligned16(data))
+        return SA_ERR_INVALID_ARG;
+    if (ntiles == 0) return SA_OK;
+    if (!data || !tiles || bytes < 2048 || bytes / 2048 > INT_MAX || ntiles > INT_MAX)
+        return SA_ERR_INVALID_ARG;
+    return to_status(sa::launch_tile_probe(data, bytes, tiles, ntiles, waves, sink,
+                                           (hipStream_t)stream));
+}
+
 const char* sa_status_string(int status) {
     switch (status) {
         case SA_OK: return "ok";

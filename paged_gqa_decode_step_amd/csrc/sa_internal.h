@@ -109,5 +109,7 @@ hipError_t launch_decode_stream(const DecodeArgs& a, bool rope, bool fused_merge
 hipError_t launch_decode_valu(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_read_probe(const void* data, size_t bytes, unsigned* sink, hipStream_t stream);
+hipError_t launch_tile_probe(const void* data, size_t bytes, const int* tiles, long long ntiles,
+                             int waves, unsigned* sink, hipStream_t stream);
 
 }  // namespace sa

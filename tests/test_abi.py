@@ -41,7 +41,7 @@ def good_dims(**kw):
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), f"{n} declared in sa.h but not exported"
     assert set(names) == set(sa.EXPORTS)
@@ -355,3 +355,16 @@ def test_noalloc_call_validates_before_touching_the_device(lib):
     assert lib.sa_decode_attention_append_noalloc(*([FAKE] * 8), 0, FAKE, ctypes.byref(big),
                                                   None) == sa.SA_ERR_SCRATCH
     assert "scratch" in sa.status_string(sa.SA_ERR_SCRATCH)
+
+
+def test_tile_probe_validates(lib):
+    sink = FAKE
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, FAKE, 10, 0, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, FAKE, 10, 65536, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, FAKE, -1, 4, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, None, 10, 4, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1024, FAKE, 10, 4, sink, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(ctypes.c_void_p(0x10008), 1 << 20, FAKE, 10, 4, sink,
+                                   None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, FAKE, 10, 4, None, None) == SA_ERR_INVALID_ARG
+    assert lib.sa_read_tiles_probe(FAKE, 1 << 20, FAKE, 0, 4, sink, None) == 0
