@@ -405,6 +405,7 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
         del g
     else:
         per_call = spread(timer.per_call_us(call, steps))
+    kernels = kernel_times_us(torch, call, steps)
     host = note = None
     if with_oracle:
         B = first.batch
@@ -415,7 +416,7 @@ def attention_config(sa, torch, timer, dev, name, steps, warmup, variant,
     e = entry(label or name, "attention", us, one, input_sets=len(sets), timing=timing,
               **({} if per_call is None else {"per_call_events": per_call}),
               splits=sa.num_splits(first.q, first.k_cache, first.v_cache, first.block_table,
-                                   first.window, variant=variant))
+                                   first.window, variant=variant), kernels_us=kernels)
     if note:
         e["oracle_sample"] = note
     del sets, outs, ws
@@ -455,6 +456,108 @@ def read_ceiling(sa, torch, timer, dev, nbytes=4 << 30):
     del x, sets
     torch.cuda.empty_cache()
     return dict(stream, scattered_tiles=tiles)
+
+
+BALANCED_WAVES = 1024       # the balanced kernel's width on calls of >= 8192 32-slot steps
+TILE_BYTES = 2048           # one (block, KV head) K or V tile: 16 slots x 64 dims x bf16
+FLOOR_TILES = 1 << 21       # 2 KiB tiles in the floor probe's 4 GiB buffer
+
+
+def layer_lens(name):
+    """(lens, window, kv_heads) of each attention layer of a named workload,
+    from its recipe (no device memory)."""
+    import synth
+    c = synth.CONFIGS[name]
+    if name == "batch64_ragged":
+        lens = (synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + 1).tolist()
+        return [(lens, w, c["kv_heads"]) for w in c["windows"]]
+    return [(list(c["lens"]), c["window"], c["kv_heads"])]
+
+
+def floor_tiles(rng, lens, window, kv_heads, balanced, splits, base=0, bs=16):
+    """The K/V tiles one attention call reads, as tile numbers in the floor
+    probe's buffer, in the order its wavefronts take them; the wavefront count;
+    and the tiles its pools span.  As in the cache, the call has a K pool and a
+    V pool of its own size (here side by side from tile ``base``), each
+    [block][KV head] tiles, so the KV heads of a block sit side by side, and
+    the sequences own the pool's blocks in a shuffled order.  Each wavefront's
+    stretch alternates a block's K and V tile.  Balanced split: the (sequence,
+    KV head) units in order, each unit's blocks in order, cut evenly over the
+    kernel's wavefronts.  Static split: partition-major, as the static
+    kernel's grid is (partition, sequence, KV head), one wavefront per
+    non-empty partition."""
+    import numpy as np
+    nb = [-(-(min(L, window) if window > 0 else L) // bs) for L in lens]
+    pool = sum(nb) * kv_heads                    # tiles in each of the two pools
+    perm = rng.permutation(sum(nb))
+    starts = np.cumsum([0] + nb)
+    seq_blocks = [perm[starts[b]:starts[b + 1]] for b in range(len(lens))]
+
+    def stretch(blocks, g):
+        k = base + blocks.astype(np.int64) * kv_heads + g
+        return np.stack([k, k + pool], axis=1).reshape(-1)
+    parts = []
+    if balanced:
+        for blocks in seq_blocks:
+            for g in range(kv_heads):
+                parts.append(stretch(blocks, g))
+        waves = BALANCED_WAVES
+    else:
+        per = -(-max(nb) // splits)
+        for sp in range(splits):
+            for blocks in seq_blocks:
+                sel = blocks[sp * per:(sp + 1) * per]
+                if len(sel):
+                    parts += [stretch(sel, g) for g in range(kv_heads)]
+        waves = len(parts)
+    return np.concatenate(parts).astype(np.int32), waves, 2 * pool
+
+
+def read_floors(sa, torch, timer, dev, specs, steps, warmup):
+    """Each call's own read floor: sa_read_tiles_probe reading exactly the
+    call's K/V tiles (floor_tiles: the cache's layout, the kernel's wavefront
+    count and order) with no arithmetic, in one launch, timed as the calls are
+    (input sets rotated past the Infinity Cache, graphs under 40 us).
+    specs: {key: (lens, window, kv_heads, balanced, splits)}."""
+    import numpy as np
+    x = torch.empty(FLOOR_TILES * TILE_BYTES, dtype=torch.uint8, device=dev)
+    x.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    rng = np.random.default_rng(11)
+    out = {}
+    for key, (lens, window, kvh, balanced, splits) in specs.items():
+        first, waves, span = floor_tiles(rng, lens, window, kvh, balanced, splits)
+        nbytes = int(first.size) * TILE_BYTES
+        nsets = 1 if nbytes > 2 * MALL_BYTES else min(64, -(-(3 * MALL_BYTES) // nbytes))
+        nsets = min(nsets, FLOOR_TILES // span)    # each set's pools in a place of their own
+        if nsets < 1:
+            raise ValueError(f"{key}: the call's pools exceed the floor buffer")
+        sets = [torch.from_numpy(first).to(dev)] + [
+            torch.from_numpy(floor_tiles(rng, lens, window, kvh, balanced, splits,
+                                         base=i * span)[0]).to(dev)
+            for i in range(1, nsets)]
+
+        def f(i=0, sets=sets, waves=waves):
+            sa.read_tiles_probe(x, sets[i % len(sets)], sink, waves=waves)
+        e = time_calls(torch, timer, [(f"read floor of {key}", nbytes, f, nsets)], steps,
+                       warmup)[0]
+        out[key] = dict(us=e["us_mean"], bytes=nbytes, wavefronts=waves, input_sets=nsets,
+                        split="balanced" if balanced else f"static, {splits} a unit",
+                        timing=e["timing"])
+        del sets
+    del x
+    torch.cuda.empty_cache()
+    return out
+
+
+def floor_fields(floor, call_us, kernel_us=None):
+    """A call's read floor beside its own times: the floor's duration over the
+    call's (and over its decode kernel's alone)."""
+    r = dict(floor, what="sa_read_tiles_probe over the call's own K/V tiles, no arithmetic",
+             call_frac=round(floor["us"] / call_us, 4))
+    if kernel_us:
+        r["kernel_frac"] = round(floor["us"] / kernel_us, 4)
+    return r
 
 
 def rope_step_config(sa, torch, timer, dev, steps, warmup, variant, with_oracle=True):
@@ -990,6 +1093,60 @@ def main():
         hosts.append(None)
         print(f"# 2-token tile: {ts['us']} us ({ts['us_one_token']} for one token), "
               f"{ts['gbps']} GB/s", flush=True)
+
+    # each dominant call's read floor: its own tiles read with no arithmetic
+    specs = {}
+
+    def add_spec(key, name, layer, splits, kernels):
+        lens, w, kvh = layer_lens(name)[layer]
+        if splits == 1:
+            balanced = False                 # one partition a unit: the static kernel
+        elif kernels:
+            balanced = "decode_stream_kernel" in kernels
+        else:
+            return
+        n = max(min(L, w) if w > 0 else L for L in lens)
+        if balanced and len(lens) * kvh * -(-n // 32) < 8 * BALANCED_WAVES:
+            return                           # a narrower balanced launch: not modelled
+        specs[key] = (lens, w, kvh, balanced, splits)
+    add_spec(args.workload + (" full layer" if args.workload == "batch64_ragged" else ""),
+             args.workload, 0, info["splits"][0], roofline.get("kernels_us"))
+    if args.workload == "batch64_ragged":
+        add_spec("batch64_ragged ring layer", "batch64_ragged", 1, info["splits"][1], None)
+    if ragged is not None:
+        add_spec("batch64_ragged full layer", "batch64_ragged", 0, ragged["splits"][0],
+                 ragged["roofline"].get("kernels_us"))
+        add_spec("batch64_ragged ring layer", "batch64_ragged", 1, ragged["splits"][1], None)
+    for e in configs:
+        if e.get("config") in ("gptoss_layer_8k", "long_131k_b1", "long_131k_b8",
+                               "long_131k_b8_tp_share"):
+            add_spec(e["config"], e["config"], 0, e["splits"], e.get("kernels_us"))
+    floors = read_floors(sa, torch, timer, dev, specs, args.steps, args.warmup)
+
+    def decode_us(kernels):
+        k = kernels or {}
+        return k.get("decode_stream_kernel") or k.get("decode_mfma_kernel")
+    main_key = args.workload + (" full layer" if args.workload == "batch64_ragged" else "")
+    if main_key in floors:
+        roofline["read_floor"] = floor_fields(floors[main_key], roofline["avg_launch_us"],
+                                              decode_us(roofline.get("kernels_us")))
+    if ragged is not None:
+        if "batch64_ragged full layer" in floors:
+            ragged["roofline"]["read_floor"] = floor_fields(
+                floors["batch64_ragged full layer"], ragged["roofline"]["avg_launch_us"],
+                decode_us(ragged["roofline"].get("kernels_us")))
+        ring = next((c for c in ragged["us_per_call"]
+                     if "attention" in c["call"] and "(w=0)" not in c["call"]), None)
+        if ring is not None and "batch64_ragged ring layer" in floors:
+            ring["read_floor"] = floor_fields(floors["batch64_ragged ring layer"],
+                                              ring["us_mean"])
+    for e in configs:
+        if e.get("config") in floors:
+            e["read_floor"] = floor_fields(floors[e["config"]], e["us"],
+                                           decode_us(e.get("kernels_us")))
+        elif e.get("config") == "batch64_8k, attention alone" and "batch64_8k" in floors:
+            e["read_floor"] = floor_fields(floors["batch64_8k"], e["us"],
+                                           decode_us(e.get("kernels_us")))
 
     # the oracle on the host's cores, after every GPU timing but the loop's
     ho = HostOracle() if oc else None

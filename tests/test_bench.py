@@ -10,6 +10,8 @@ import os
 import subprocess
 import sys
 
+import numpy as np
+
 import bench
 import synth
 
@@ -83,3 +85,70 @@ def test_oracle_task_runs_the_oracle_on_its_share(tmp_path):
     k, v = oracle.kv_append(h["k"], h["v"], h["kn"], h["vn"], h["bt"], h["lens"], 0)
     want = oracle.decode_attention(h["q"], k, v, h["bt"], h["lens"], h["sinks"], 0)
     assert np.array_equal(got, want[[0, 2]][:, 4:8])      # KV head 1: query heads 4..7
+
+
+def _check_floor_tiles(lens, window, kvh, balanced, splits):
+    import numpy as np
+    base = 1000
+    t, waves, span = bench.floor_tiles(np.random.default_rng(5), lens, window, kvh, balanced,
+                                       splits, base=base)
+    nb = [-(-(min(L, window) if window > 0 else L) // 16) for L in lens]
+    pool = sum(nb) * kvh
+    assert span == 2 * pool
+    k, v = t[0::2].astype(np.int64) - base, t[1::2].astype(np.int64) - base
+    # a block's K tile, then its V tile at the same place in the V pool that
+    # follows the K pool
+    assert (k >= 0).all() and (k < pool).all() and np.array_equal(v, k + pool)
+    # every (block, KV head) tile of the pools exactly once
+    assert len(np.unique(k)) == len(k) == pool
+    return k, waves
+
+
+def test_floor_tiles_balanced_follow_the_units_in_order():
+    lens = [40, 700, 3001, 16]
+    k, waves = _check_floor_tiles(lens, 0, 4, True, 8)
+    assert waves == bench.BALANCED_WAVES
+    # unit (b, g): its blocks for head g, then the next unit
+    nb = [3, 44, 188, 1]
+    at = 0
+    for b in range(4):
+        blocks = None
+        for g in range(4):
+            seg = k[at:at + nb[b]]
+            assert (seg % 4 == g).all()
+            if blocks is None:
+                blocks = seg // 4
+            assert np.array_equal(seg // 4, blocks)      # the same blocks for every head
+            at += nb[b]
+    assert at == len(k)
+
+
+def test_floor_tiles_static_one_partition_a_wavefront():
+    import numpy as np
+    # 2 sequences of 8192, 8 KV heads, 32 partitions: 512 wavefronts of 16 blocks
+    k, waves = _check_floor_tiles([8192, 8192], 0, 8, False, 32)
+    assert waves == 32 * 2 * 8
+    per = len(k) // waves
+    assert per == 16
+    for w in range(waves):
+        seg = k[w * per:(w + 1) * per]
+        assert (seg % 8 == w % 8).all()                  # partition-major, head innermost
+    # a ring layer: the window's blocks only
+    k, waves = _check_floor_tiles([5000, 129], 128, 8, False, 1)
+    assert waves == 16 and len(k) == 2 * 8 * 8
+
+
+def test_balanced_width_matches_the_library():
+    import re
+    with open(os.path.join(ROOT, "paged_gqa_decode_step_amd", "csrc", "plan.h")) as f:
+        m = re.search(r"#define SA_STREAM_WAVES (\d+)", f.read())
+    assert int(m.group(1)) == bench.BALANCED_WAVES
+
+
+def test_layer_lens_match_the_workloads():
+    c = synth.CONFIGS["batch64_ragged"]
+    lens = synth.ragged_lengths(c["seed"], c["batch"], *c["len_range"]) + 1
+    layers = bench.layer_lens("batch64_ragged")
+    assert [w for _, w, _ in layers] == [0, 128]
+    assert layers[0][0] == lens.tolist()
+    assert bench.layer_lens("long_131k_b8_tp_share") == [([131072] * 8, 0, 1)]
