@@ -18,8 +18,8 @@ namespace {
 
 using namespace mfma;
 
-// DEPTH: the step pipeline (2, or kBurst: every step of a partition of at
-// most kBurst steps loaded at once).
+// DEPTH: the step pipeline (2), or a burst (4 or kBurst: every step of a
+// partition of at most DEPTH steps loaded at once).
 template <int BSL, bool ROPE, bool MULTI, int DEPTH>
 __global__ __launch_bounds__(64) void decode_mfma_kernel(const DecodeArgs a) {
     const int lane = threadIdx.x;
@@ -142,9 +142,12 @@ hipError_t launch_static_depth(const DecodeArgs& a, bool rope, hipStream_t strea
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, bool burst, hipStream_t stream) {
-    return burst ? launch_static_depth<kBurst>(a, rope, stream)
-                 : launch_static_depth<2>(a, rope, stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, int depth, hipStream_t stream) {
+    switch (depth) {
+        case kBurst: return launch_static_depth<kBurst>(a, rope, stream);
+        case 4: return launch_static_depth<4>(a, rope, stream);
+        default: return launch_static_depth<2>(a, rope, stream);
+    }
 }
 
 }  // namespace sa

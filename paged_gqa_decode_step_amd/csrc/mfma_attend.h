@@ -517,21 +517,21 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
         }
     }
 
-    if constexpr (DEPTH == kBurst) {
-        // Runs of up to kBurst steps issue every step's loads at once (steps
+    if constexpr (DEPTH == kBurst || DEPTH == 4) {
+        // Runs of up to DEPTH steps issue every step's loads at once (steps
         // past the run re-read its last chunk, which the clamp in load_step
         // keeps inside the run's blocks, and are never computed): one round
         // trip of K/V instead of a pipeline's several, for calls whose
         // partitions are short.  Longer runs take the two-step pipeline.
-        if (nsteps <= kBurst) {
-            StepRegs R[kBurst];
+        if (nsteps <= DEPTH) {
+            StepRegs R[DEPTH];
             load_step(0, R[0]);
             if (stores_new && !new_first) store_new();
 #pragma unroll
-            for (int s = 1; s < kBurst; ++s) load_step(s, R[s]);
+            for (int s = 1; s < DEPTH; ++s) load_step(s, R[s]);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int s = 0; s < kBurst; ++s)
+            for (int s = 0; s < DEPTH; ++s)
                 if (s < nsteps) compute_step(s, R[s]);
             return;
         }
@@ -628,7 +628,8 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
 // blocks (t0 a multiple of 32).  The first run's table slice and the new
 // token's words are read here, with no branch, so they travel with the
 // caller's query loads.
-// DEPTH: register sets of the step pipeline (2, or 3 for one wavefront per SIMD).
+// DEPTH: register sets of the step pipeline (2, or 3 for one wavefront per SIMD),
+// or a burst's (4 or kBurst: a run of at most DEPTH steps loaded at once).
 // The loads that begin a unit's run of slots from t0: its first table slice
 // and this lane's words of the new token's K and V rows.  None of them
 // depends on the sequence's length, so a caller may issue them before it

@@ -135,20 +135,29 @@ long stream_waves(const sa_dims* d, int32_t window) {
     return nw < 1 ? 1 : nw;
 }
 
-// The static kernel loads every step of its partition at once when
-// partitions are kBurstSteps steps and the grid is at most one
-// wavefront per SIMD (the burst kernels hold all those steps in registers,
-// so they run one wavefront per SIMD): one round trip of K/V per partition,
-// for calls too small to keep HBM busy with pipelined wavefronts.
+// The static kernel loads every step of its partition at once (a burst)
+// when partitions are exactly kBurstSteps or 4 steps and the grid is at most
+// one wavefront per SIMD (the burst kernels hold all those steps in
+// registers, so they run one wavefront per SIMD): one round trip of K/V per
+// partition, for calls too small to keep HBM busy with pipelined
+// wavefronts.  The burst covers exactly the partition's steps: the 8-step
+// burst on the ring layer's 4-step partitions, with four unused loads each,
+// measured slower than the pipeline (7.40 vs 6.59 us), the 4-step burst
+// faster (6.43 vs 6.53 us, bit-identical output).  Returns the register
+// depth: kBurstSteps or 4 for a burst, 2 for the two-step pipeline.
 #ifndef SA_STATIC_BURST
 #define SA_STATIC_BURST 1
 #endif
+int static_depth(const sa_dims* d, const Plan& p) {
+    if (!SA_STATIC_BURST ||
+        (long long)d->num_seqs * d->num_kv_heads * p.splits > kStreamWaves)
+        return 2;
+    if (p.part_tokens == sa::kBurstSteps * sa::kStepTokens) return sa::kBurstSteps;
+    if (p.part_tokens == 4 * sa::kStepTokens) return 4;
+    return 2;
+}
 bool static_burst(const sa_dims* d, const Plan& p) {
-    if (!SA_STATIC_BURST) return false;
-    // exactly kBurstSteps steps a partition: shorter ones (the ring layer's
-    // 4) measured slower with the burst's unused loads than pipelined
-    return p.part_tokens == sa::kBurstSteps * sa::kStepTokens &&
-           (long long)d->num_seqs * d->num_kv_heads * p.splits <= kStreamWaves;
+    return static_depth(d, p) == sa::kBurstSteps;
 }
 
 // Which kernel a call with these dims uses (assumes check_dims passed).

@@ -157,10 +157,10 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     if (!grid_fits(dims, p.splits)) return SA_ERR_INVALID_ARG;
     const Mode mode = choose_mode(dims, window, p);
     const bool with_rope = rope != nullptr;
-    const bool burst = static_burst(dims, p);
-    auto launch_static = [valu, with_rope, burst](const sa::DecodeArgs& args, hipStream_t strm) {
+    const int depth = static_depth(dims, p);
+    auto launch_static = [valu, with_rope, depth](const sa::DecodeArgs& args, hipStream_t strm) {
         return valu ? sa::launch_decode_valu(args, strm)
-                    : sa::launch_decode_mfma(args, with_rope, burst, strm);
+                    : sa::launch_decode_mfma(args, with_rope, depth, strm);
     };
     const WorkspaceLayout wl = workspace_layout(dims, window, p, mode);
     if (lib_scratch) {
@@ -217,7 +217,7 @@ int decode(const sa_bf16* q, const sa_bf16* k_new, const sa_bf16* v_new,
     a.counters = (int32_t*)(ws + wl.counters);
     if (mode == Mode::kFused) {
         a.mode = sa::kFusedCombine;
-        return to_status(sa::launch_decode_mfma(a, with_rope, burst, s));
+        return to_status(sa::launch_decode_mfma(a, with_rope, depth, s));
     }
     a.mode = sa::kWritePartials;
     st = to_status(launch_static(a, s));
@@ -308,7 +308,7 @@ int sa_decode_partials(const sa_bf16* q, const sa_bf16* k_cache, const sa_bf16* 
     a.part_o = part_o;
     a.part_lse = part_lse;
     a.mode = sa::kWritePartials;
-    return to_status(sa::launch_decode_mfma(a, false, static_burst(dims, p), (hipStream_t)stream));
+    return to_status(sa::launch_decode_mfma(a, false, static_depth(dims, p), (hipStream_t)stream));
 }
 
 int sa_combine(const float* part_o, const float* part_lse, const float* sinks,

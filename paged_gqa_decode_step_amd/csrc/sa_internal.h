@@ -100,7 +100,7 @@ hipError_t launch_kv_append(const AppendArgs& a, hipStream_t stream);
 // the kernels built for several causal query tokens per sequence
 // burst: the kernels that load every step of a partition of at most 8 steps
 // at once (for grids of short partitions)
-hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, bool burst, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeArgs& a, bool rope, int depth, hipStream_t stream);
 // fused_merge: the last wavefront of a split unit merges it (part_o holds the
 // segments, counters the arrivals); otherwise a merge launch follows, reading
 // part_o / part_lse and the unit records in unit_seg
