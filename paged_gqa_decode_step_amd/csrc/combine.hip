@@ -23,7 +23,6 @@ namespace sa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kOneWaveSplits = 8;   // partitions up to which one wavefront merges a row
 
 template <int WAVES, int CHUNK>
 __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a) {
@@ -108,10 +107,10 @@ __global__ __launch_bounds__(64 * WAVES) void combine_kernel(const CombineArgs a
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
     const dim3 grid((unsigned)a.B * a.Hq);
-    if (a.num_splits <= kOneWaveSplits)
-        return launch(combine_kernel<1, kOneWaveSplits>, grid, dim3(64), 0, stream, a);
-    else if (a.num_splits <= 64)
-        return launch(combine_kernel<4, 16>, grid, dim3(256), 0, stream, a);
+    if (a.num_splits <= kCombineOneWave)
+        return launch(combine_kernel<1, kCombineOneWave>, grid, dim3(64), 0, stream, a);
+    else if (a.num_splits <= kCombineFourWaves)
+        return launch(combine_kernel<4, kCombineFourWaves / 4>, grid, dim3(256), 0, stream, a);
     else
         return launch(combine_kernel<16, 16>, grid, dim3(1024), 0, stream, a);
 }

@@ -79,12 +79,28 @@ Plan plan(const sa_dims* d, int32_t window) {
         while (P / 2 >= gran && P / 2 >= kMinPartTokens &&
                units * ((max_n + P - 1) / P) < kMinWaves)
             P /= 2;
-        // a call that is split anyway takes burst partitions when their grid
-        // fits (a call of one partition a unit needs no merge at all)
+        // A call that is split anyway takes burst partitions when their grid
+        // fits (a call of one partition a unit needs no merge at all): of 4
+        // steps when that grid fits too, keeps the merge to at most
+        // kCombineFourWaves partials a row, and leaves the one-wavefront
+        // merge (kCombineOneWave partials) only for a grid of fewer than half
+        // the wavefronts; else of 8 steps.  Measured on MI355X (us, 8-step vs
+        // 4-step partitions): batch 1 x 1024 6.92 / 5.87, 1 x 4096 7.95 /
+        // 7.13, 1 x 8192 8.47 / 8.27, 2 x 2048 7.43 / 7.09, 2 x 8192 11.61 /
+        // 11.34, 4 x 4096 11.54 / 11.29; kept at 8 steps: 8 x 2048 11.24 /
+        // 11.57 (the wider merge), 1 x 16384 11.71 / 12.30 (128 partials a
+        // row).
         const int pb = sa::kBurstSteps * sa::kStepTokens;
+        const int p4 = 4 * sa::kStepTokens;
         if (max_n > P && pb >= gran && pb <= pmax &&
-            units * ((max_n + pb - 1) / pb) <= kStreamWaves)
+            units * ((max_n + pb - 1) / pb) <= kStreamWaves) {
+            const long s8 = (max_n + pb - 1) / pb, s4 = (max_n + p4 - 1) / p4;
             P = pb;
+            if (p4 >= gran && units * s4 <= kStreamWaves && s4 <= sa::kCombineFourWaves &&
+                (s4 <= sa::kCombineOneWave || s8 > sa::kCombineOneWave ||
+                 units * s8 < kStreamWaves / 2))
+                P = p4;
+        }
     }
     Plan p;
     p.part_tokens = P;

@@ -24,6 +24,11 @@ constexpr int kMaxGroup = 16;      // query columns per KV head: (query tokens) 
 constexpr int kStepTokens = 32;    // tokens per inner step of the partition kernels
 constexpr int kMaxTableSlice = 64; // block-table entries one partition may span
 constexpr int kBurstSteps = 8;     // steps of a partition the burst kernels load at once
+// widths of the static merge (combine_kernel): one wavefront merges a row of
+// up to kCombineOneWave partials, four wavefronts up to kCombineFourWaves,
+// sixteen any more
+constexpr int kCombineOneWave = 8;
+constexpr int kCombineFourWaves = 64;
 
 struct AppendArgs {
     const uint16_t* k_new;

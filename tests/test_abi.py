@@ -262,10 +262,13 @@ def test_binding_checks_the_pool_layouts():
 
 
 def test_small_grids_of_few_partitions_take_the_static_split(lib):
-    """A static grid of 8-step partitions that fits one wavefront per SIMD, or
-    of 512 to 1024 partitions, runs the static split (its workspace holds S
-    partials for every output row); any other grid, the balanced kernel (two
-    partial slots per wavefront of 1024)."""
+    """A static grid of burst partitions (4 or 8 steps) that fits one
+    wavefront per SIMD, or of 512 to 1024 partitions, runs the static split
+    (its workspace holds S partials for every output row); any other grid,
+    the balanced kernel (two partial slots per wavefront of 1024).  Burst
+    partitions are of 4 steps when that grid fits too, a row keeps at most 64
+    partials, and a row passes 8 partials only where the 8-step grid holds
+    fewer than 512 wavefronts."""
     counters = (1 << 18) * 4
 
     def ws(B, mbs, S, variant=0):
@@ -290,12 +293,15 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
     assert ws(64, 128, 2) == static(64, 2)               # 1024 partitions
     assert ws(8, 512, 8) == static(8, 8)                 # 512
 
-    assert ws(1, 512, 32) == static(1, 32)               # 256: batch 1 x 8192
+    assert ws(1, 512, 64) == static(1, 64)               # 512 of 4 steps: batch 1 x 8192
     assert ws(1, 8192, 128) == static(1, 128)            # 1024: batch 1 x 131072
     assert ws(128, 128, 2) == balanced(128)              # 2048
-    assert ws(1, 128, 8) == static(1, 8)                 # 64 burst partitions
-    assert ws(2, 512, 32) == static(2, 32)               # 512 burst partitions
-    assert ws(4, 512, 32) == static(4, 32)               # 1024 burst partitions
+    assert ws(1, 128, 16) == static(1, 16)               # 128 of 4 steps (8-step grid: 64)
+    assert ws(2, 512, 64) == static(2, 64)               # 1024 of 4 steps
+    assert ws(4, 512, 32) == static(4, 32)               # 1024 of 8 steps (4 steps: 2048)
+    assert ws(1, 1024, 64) == static(1, 64)              # 512 of 8 steps (4 steps: 128 a row)
+    assert ws(8, 128, 8) == static(8, 8)                 # 512 of 8 steps: one-wavefront merge kept
+    assert ws(2, 128, 16) == static(2, 16)               # 256 of 4 steps (8-step grid: 128)
     assert ws(3, 1024, 16) == balanced(3)                # 384 partitions of 32 steps
     assert ws(128, 128, 2, variant=5) == balanced_last_merges(128)
     assert ws(4, 512, 32, variant=4) == balanced(4)
