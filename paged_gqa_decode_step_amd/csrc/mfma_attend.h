@@ -497,23 +497,35 @@ __device__ __forceinline__ void attend_run(const Unit& u, int t0, int t1, int tb
     const bool stores_new = has_new && nblk_ok;                  // wave-uniform
     const bool new_first = stores_new && u.new_slot < t0 + kStepTokens;
     if (new_first) store_new();
-    if (MULTI && u.appends) {
-        // every new token whose slot lies in this run, before any load
-        for (int t = 0; t < u.T; ++t) {
-            const int slot = u.L - u.T + t;                  // wave-uniform
-            if (slot < t0 || slot >= t1) continue;
-            const int lane = c16 + 16 * q4;
-            const unsigned nb =
-                (unsigned)__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl);
-            if (!__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl_ok)) continue;
-            const unsigned noff = (unsigned)(slot & (bs - 1));
-            const size_t off = (size_t)nb * u.blk_stride;
-            const unsigned kw =
-                reinterpret_cast<const unsigned*>(u.kn_row + (size_t)t * u.kn_stride)[lane & 31];
-            const uint16_t vv = (u.vn_row + (size_t)t * u.kn_stride)[lane];
-            *reinterpret_cast<uint16_t*>(u.vstore + off + v_elem_offset(noff, lane)) = vv;
-            *reinterpret_cast<unsigned*>(u.kstore + off + k_word_offset<bs>(noff, lane & 31)) =
-                kw;
+    if (MULTI && u.appends && u.L - 1 >= t0 && u.L - u.T < t1) {
+        // every new token whose slot lies in this run, before any load.  The
+        // words of up to kAppendGroup tokens are read together (unconditional
+        // loads: past the last token they re-read it), so a group costs one
+        // round trip, not one per token.
+        constexpr int kAppendGroup = 4;
+        const int lane = c16 + 16 * q4;
+        for (int tg = 0; tg < u.T; tg += kAppendGroup) {
+            unsigned kws[kAppendGroup];
+            uint16_t vvs[kAppendGroup];
+#pragma unroll
+            for (int j = 0; j < kAppendGroup; ++j) {
+                const size_t row = (size_t)min(tg + j, u.T - 1) * u.kn_stride;
+                kws[j] = reinterpret_cast<const unsigned*>(u.kn_row + row)[lane & 31];
+                vvs[j] = (u.vn_row + row)[lane];
+            }
+#pragma unroll
+            for (int j = 0; j < kAppendGroup; ++j) {
+                const int slot = u.L - u.T + tg + j;         // wave-uniform
+                if (tg + j >= u.T || slot < t0 || slot >= t1) continue;
+                const unsigned nb =
+                    (unsigned)__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl);
+                if (!__builtin_amdgcn_ds_bpermute(((slot >> BSL) - blk0) << 2, tbl_ok)) continue;
+                const unsigned noff = (unsigned)(slot & (bs - 1));
+                const size_t off = (size_t)nb * u.blk_stride;
+                *reinterpret_cast<uint16_t*>(u.vstore + off + v_elem_offset(noff, lane)) = vvs[j];
+                *reinterpret_cast<unsigned*>(u.kstore + off +
+                                             k_word_offset<bs>(noff, lane & 31)) = kws[j];
+            }
         }
     }
 
