@@ -152,3 +152,12 @@ def test_layer_lens_match_the_workloads():
     assert [w for _, w, _ in layers] == [0, 128]
     assert layers[0][0] == lens.tolist()
     assert bench.layer_lens("long_131k_b8_tp_share") == [([131072] * 8, 0, 1)]
+
+
+def test_floor_tiles_refuse_pools_past_the_buffer():
+    import pytest
+    with pytest.raises(ValueError):
+        bench.floor_tiles(np.random.default_rng(0), [bench.FLOOR_TILES * 16], 0, 1, True, 8)
+    t, waves, span = bench.floor_tiles(np.random.default_rng(0), [1024], 0, 8, True, 8,
+                                       base=bench.FLOOR_TILES - 1024)
+    assert span == 1024 and t.max() < bench.FLOOR_TILES
