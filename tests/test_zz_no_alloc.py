@@ -57,3 +57,36 @@ def test_noalloc_equals_workspace_call(lib, case, variant):
         assert torch.equal(out, want), f"{what}: output differs"
         assert torch.equal(a.k_cache, b.k_cache), f"{what}: K pool differs"
         assert torch.equal(a.v_cache, b.v_cache), f"{what}: V pool differs"
+
+
+def tile_pair(batch, lens, T, q_heads, seed):
+    """Two identical copies of a layer with a query tile of T tokens (the
+    tile's K/V rows appended inside the call)."""
+    a, b = layer_pair(batch=batch, q_heads=q_heads, kv_heads=8, head_dim=64, block_size=16,
+                      lens=lens, seed=seed)
+    g = torch.Generator(device="cuda").manual_seed(seed + 1)
+    q = torch.randn(batch, T, q_heads, 64, generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(batch, T, 8, 64, generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn(batch, T, 8, 64, generator=g, device="cuda").to(torch.bfloat16)
+    return a, b, q, kn, vn
+
+
+@pytest.mark.parametrize("variant", [0, 2, 5])
+def test_noalloc_query_tile_equals_workspace_call(lib, variant):
+    """Query tiles through the no-allocation call: batch 64 ragged with 2
+    tokens, then batch 8 with 4 tokens (32 query heads, so the tile still
+    fills 16 columns); bit-identical to the workspace call."""
+    calls = ((64, (synth.ragged_lengths(75, 64, 513, 8193) + 2).tolist(), 2, 64),
+             (8, (synth.ragged_lengths(76, 8, 4, 3000) + 4).tolist(), 4, 32))
+    for i, (B, lens, T, hq) in enumerate(calls):
+        a, b, q, kn, vn = tile_pair(B, lens, T, hq, seed=5200 + 10 * i + variant)
+        want = lib.decode_attention_append(q, kn, vn, a.k_cache, a.v_cache, a.block_table,
+                                           a.seq_lens, a.sinks[:hq], 0, variant=variant)
+        out = torch.full_like(q, float("nan"))
+        lib.decode_attention_append_noalloc(q, kn, vn, b.k_cache, b.v_cache, b.block_table,
+                                            b.seq_lens, out, b.sinks[:hq], 0, variant=variant)
+        torch.cuda.synchronize()
+        what = f"tile call {i} (T={T}) variant {variant}"
+        assert torch.equal(out, want), f"{what}: output differs"
+        assert torch.equal(a.k_cache, b.k_cache), f"{what}: K pool differs"
+        assert torch.equal(a.v_cache, b.v_cache), f"{what}: V pool differs"
