@@ -174,22 +174,24 @@ def test_fused_decode_loop_sampled(lib):
         assert np.array_equal(now["k"], host[li]["k"]) and np.array_equal(now["v"], host[li]["v"])
 
 
+@pytest.mark.parametrize("variant", [0, 1, 2])
 @pytest.mark.parametrize("W", [0, 500])
 @pytest.mark.parametrize("part", [0, 128, 256])
-def test_burst_partitions_with_the_append(lib, W, part):
+def test_burst_partitions_with_the_append(lib, W, part, variant):
     """Calls small enough for burst partitions (every step loaded at once): of
     4 steps (128 slots, the plan's choice here: part 0) and of 8 (256 slots,
     forced through the split count); the new token at a partition's first,
     last and next-to-last slot, short last partitions, a ring wider than one
     partition; pools bit for bit and the output against the oracle, plain and
-    fused."""
+    fused; the default launch, the static two-pass split and the static split
+    whose last partition merges (variants 0, 1, 2)."""
     lens = [1, 127, 128, 129, 255, 256, 257, 511, 512, 513, 1000]
     layer = synth.make_layer(batch=len(lens), q_heads=64, kv_heads=8, head_dim=64,
                              block_size=16, lens=lens, window=W, seed=9900 + W, device="cuda")
     n_max = min(W, 1008) if W > 0 else 1008              # 63 blocks of capacity
     forced = -(-n_max // part) if part else 0
     S = lib.num_splits(layer.q, layer.k_cache, layer.v_cache, layer.block_table, W,
-                       num_splits=forced)
+                       num_splits=forced, variant=variant)
     assert S == -(-n_max // (part or 128)), "partitions of the intended length"
     assert len(lens) * 8 * S <= 1024, "a grid the burst kernels take"
     s = sub_layer(layer, range(layer.batch))
@@ -198,14 +200,15 @@ def test_burst_partitions_with_the_append(lib, W, part):
     kc, vc = layer.k_cache.clone(), layer.v_cache.clone()
     out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, kc, vc,
                                       layer.block_table, layer.seq_lens, layer.sinks, W,
-                                      num_splits=forced)
+                                      num_splits=forced, variant=variant)
     torch.cuda.synchronize()
     after = sub_layer(dataclasses.replace(layer, k_cache=kc, v_cache=vc), range(layer.batch))
     assert np.array_equal(after["k"], kr) and np.array_equal(after["v"], vr)
-    assert_parity(out_f64(out), ref, f"burst W={W} part={part} fused")
+    assert_parity(out_f64(out), ref, f"burst W={W} part={part} v={variant} fused")
     lib.kv_append(layer.k_new, layer.v_new, layer.k_cache, layer.v_cache, layer.block_table,
                   layer.seq_lens, W)
     plain = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
-                                 layer.seq_lens, layer.sinks, W, num_splits=forced)
+                                 layer.seq_lens, layer.sinks, W, num_splits=forced,
+                                 variant=variant)
     torch.cuda.synchronize()
     assert torch.equal(plain, out), "fused and append-then-attend differ"
