@@ -136,3 +136,39 @@ def test_decode_loop_sampled(lib):
     for li, m in enumerate(model):
         now = sub_layer(m, seqs)
         assert np.array_equal(now["k"], host[li]["k"]) and np.array_equal(now["v"], host[li]["v"])
+
+
+@pytest.mark.parametrize("variant", [0, 5])
+@pytest.mark.parametrize("shape", ["batch64_8k", "batch64_ragged"])
+def test_full_size_calls_repeat_bit_for_bit(lib, shape, variant):
+    """Races in the merge across wavefronts (units split over wavefronts, the
+    merge launch or the last-arriving wavefront's merge) would show as runs
+    that differ: five calls at full size through one reused workspace, each
+    bit-identical to the first, the attention alone and with the append."""
+    layer = (synth.make_layer(device="cuda", **synth.CONFIGS["batch64_8k"])
+             if shape == "batch64_8k" else ragged_layers()[0])
+    ws = lib.new_workspace(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                           layer.window, variant=variant)
+    first = None
+    for i in range(5):
+        out = lib.decode_attention(layer.q, layer.k_cache, layer.v_cache, layer.block_table,
+                                   layer.seq_lens, layer.sinks, layer.window, workspace=ws,
+                                   variant=variant)
+        torch.cuda.synchronize()
+        if first is None:
+            first = out.clone()
+        assert torch.equal(out, first), f"{shape} v={variant}: run {i} differs from run 0"
+    # the fused step: its append is idempotent here (the same rows into the
+    # same slots), so every run sees the same pools
+    fused0 = None
+    for i in range(3):
+        out = lib.decode_attention_append(layer.q, layer.k_new, layer.v_new, layer.k_cache,
+                                          layer.v_cache, layer.block_table, layer.seq_lens,
+                                          layer.sinks, layer.window, workspace=ws,
+                                          variant=variant)
+        torch.cuda.synchronize()
+        if fused0 is None:
+            fused0 = out.clone()
+            k1, v1 = layer.k_cache.clone(), layer.v_cache.clone()
+        assert torch.equal(out, fused0), f"{shape} v={variant}: fused run {i} differs"
+        assert torch.equal(layer.k_cache, k1) and torch.equal(layer.v_cache, v1)
