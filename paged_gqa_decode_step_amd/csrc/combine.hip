@@ -112,7 +112,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
     else if (a.num_splits <= kCombineFourWaves)
         return launch(combine_kernel<4, kCombineFourWaves / 4>, grid, dim3(256), 0, stream, a);
     else
-        return launch(combine_kernel<16, 16>, grid, dim3(1024), 0, stream, a);
+        return launch(combine_kernel<8, 16>, grid, dim3(512), 0, stream, a);
 }
 
 }  // namespace sa
