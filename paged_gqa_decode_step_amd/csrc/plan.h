@@ -90,6 +90,19 @@ Plan plan(const sa_dims* d, int32_t window) {
         // 11.34, 4 x 4096 11.54 / 11.29; kept at 8 steps: 8 x 2048 11.24 /
         // 11.57 (the wider merge), 1 x 16384 11.71 / 12.30 (128 partials a
         // row).
+        // The widest merges (more than kCombineFourWaves partials a row) on a
+        // static grid of half to one wavefront per SIMD: partitions of two
+        // table slices halve the partials and keep half the SIMDs or more
+        // busy (measured: batch 1 x 131072 45.53 -> 44.94 us, its
+        // tensor-parallel share 45.64 -> 45.12).  The static MFMA kernel
+        // walks a partition's slices in turn; the vector-ALU engine reads one
+        // slice a partition, so it keeps them.
+        {
+            const long s1 = (max_n + P - 1) / P, s2 = (max_n + 2L * P - 1) / (2L * P);
+            if (P == pmax && d->variant != SA_VARIANT_VALU && s1 > sa::kCombineFourWaves &&
+                units * s1 <= kStreamWaves && 2 * units * s2 >= kStreamWaves)
+                P *= 2;
+        }
         const int pb = sa::kBurstSteps * sa::kStepTokens;
         const int p4 = 4 * sa::kStepTokens;
         if (max_n > P && pb >= gran && pb <= pmax &&

@@ -294,7 +294,9 @@ def test_small_grids_of_few_partitions_take_the_static_split(lib):
     assert ws(8, 512, 8) == static(8, 8)                 # 512
 
     assert ws(1, 512, 64) == static(1, 64)               # 512 of 4 steps: batch 1 x 8192
-    assert ws(1, 8192, 128) == static(1, 128)            # 1024: batch 1 x 131072
+    assert ws(1, 8192, 64) == static(1, 64)              # 512 of 2048 slots: batch 1 x 131072
+    assert ws(1, 8192, 128, variant=3) == static(1, 128)  # the vector-ALU engine: 1024 slots
+    assert ws(1, 4096, 64) == static(1, 64)              # 1 x 65536: 64 partials, 1024 slots
     assert ws(128, 128, 2) == balanced(128)              # 2048
     assert ws(1, 128, 16) == static(1, 16)               # 128 of 4 steps (8-step grid: 64)
     assert ws(2, 512, 64) == static(2, 64)               # 1024 of 4 steps
